@@ -1,0 +1,253 @@
+/*
+ * tern_oracle.c -- plain, slow, FP64 reference for the ternary-g128 matmul
+ * and the signed normalized Walsh-Hadamard rotation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's library.  It shares no
+ * code, header, table or constant with the HIP library and includes nothing
+ * from it.  Every function is the definition written out, in the order the
+ * sources state it, with no blocking, fusion or reordering.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [MC]  "prism-ml/Ternary-Bonsai-27B-mlx-2bit" model card,
+ *        sections "Weight representation: ternary g128", "Memory requirement",
+ *        "CUDA (NVIDIA GPUs)".
+ *  [9B]  "Ternary-Bonsai-2-9B-2bit" article, section 3
+ *        "Ternary weights and Hadamard rotation".
+ *
+ * Readings where the sources are silent (each is listed in the design notes):
+ *  - slot code q = t + 1 in {0,1,2}; 16 slots per little-endian uint32,
+ *    K-major, slot j of word w holds k = 16 w + j at bits 2j..2j+1;
+ *  - scales are IEEE binary16, one per 128 consecutive K of one output row;
+ *  - the Hadamard matrix is in natural (Sylvester) order,
+ *    H[i][l] = (-1)^popcount(i & l), normalized by 1/sqrt(b), applied to
+ *    contiguous blocks of b along the last dimension, signs first.
+ *
+ * Parity pins: every function here is pinned by tests/test_oracle_pins.py
+ * (closed forms, invariants, library routines, brute force); none is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define ORACLE_GROUP 128   /* [MC] Weight representation: 128 weights per FP16 scale */
+#define ORACLE_SLOTS 16    /* 2-bit slots per 32-bit word ([MC] Memory requirement) */
+
+/* IEEE 754 binary16 -> double, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)            /* zero or subnormal: f * 2^-24 */
+        v = ldexp((double)f, -24);
+    else if (e == 31)      /* infinity or NaN */
+        v = (f == 0) ? INFINITY : NAN;
+    else                   /* normal: (1 + f/1024) * 2^(e-15) */
+        v = ldexp(1.0 + (double)f / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t b)
+{
+    union { uint32_t u; float f; } cvt;
+    cvt.u = (uint32_t)b << 16;
+    return (double)cvt.f;
+}
+
+/* Activation element (m, k) as a double; xdt 0 = binary32, 1 = bfloat16,
+ * 2 = binary64. */
+static double x_at(const void *x, int xdt, int64_t K, int64_t m, int64_t k)
+{
+    int64_t i = m * K + k;
+    if (xdt == 0) return (double)((const float *)x)[i];
+    if (xdt == 1) return oracle_bf16_to_double(((const uint16_t *)x)[i]);
+    return ((const double *)x)[i];
+}
+
+/* Ternary value of weight (n, k) from its 2-bit slot: t = q - 1.
+ * Returns 2 for the unused slot value q = 3 (not a ternary code). */
+static int slot_t(const uint32_t *codes, int64_t K, int64_t n, int64_t k, int *t)
+{
+    int64_t words_per_row = K / ORACLE_SLOTS;
+    uint32_t w = codes[n * words_per_row + k / ORACLE_SLOTS];
+    int q = (int)((w >> (2 * (k % ORACLE_SLOTS))) & 3u);
+    if (q == 3) return 2;
+    *t = q - 1;
+    return 0;
+}
+
+/* Decode every slot into t in {-1,0,+1}.  Returns 0, or 3 if a slot holds 3. */
+int oracle_decode(const uint32_t *codes, int64_t N, int64_t K, int8_t *t)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int v;
+            if (slot_t(codes, K, n, k, &v)) return 3;
+            t[n * K + k] = (int8_t)v;
+        }
+    return 0;
+}
+
+/* Encode t in {-1,0,+1} into 2-bit slots q = t + 1.  Returns 0, or 2 if some
+ * t is not ternary.  codes must hold N*K/16 words. */
+int oracle_encode(const int8_t *t, int64_t N, int64_t K, uint32_t *codes)
+{
+    int64_t words = N * (K / ORACLE_SLOTS);
+    for (int64_t i = 0; i < words; ++i) codes[i] = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int v = t[n * K + k];
+            if (v < -1 || v > 1) return 2;
+            uint32_t q = (uint32_t)(v + 1);
+            codes[n * (K / ORACLE_SLOTS) + k / ORACLE_SLOTS] |= q << (2 * (k % ORACLE_SLOTS));
+        }
+    return 0;
+}
+
+/* Dequantized weight w = s_g * t, with s_g the scale of the group of 128
+ * consecutive K that k falls in ([MC] Weight representation).  Exact in
+ * double: a binary16 times -1, 0 or +1. */
+static double weight(const uint32_t *codes, const uint16_t *scales, int64_t K,
+                     int64_t n, int64_t k, int *bad)
+{
+    int t;
+    if (slot_t(codes, K, n, k, &t)) { *bad = 1; return 0.0; }
+    double s = oracle_half_to_double(scales[n * (K / ORACLE_GROUP) + k / ORACLE_GROUP]);
+    return s * (double)t;
+}
+
+/* One output: y = sum_k w[n][k] * x[m][k] and the error scale
+ * B = sum_k |w[n][k] * x[m][k]|, summed in k order in double. */
+static int one_output(const void *x, int xdt, int64_t K, const uint32_t *codes,
+                      const uint16_t *scales, int64_t m, int64_t n,
+                      double *y, double *bound)
+{
+    double acc = 0.0, b = 0.0;
+    int bad = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = weight(codes, scales, K, n, k, &bad) * x_at(x, xdt, K, m, k);
+        acc += p;
+        b += fabs(p);
+    }
+    *y = acc;
+    *bound = b;
+    return bad ? 3 : 0;
+}
+
+/* y[m][n] = sum_k (s_g t)[n][k] x[m][k] for all m < M, n < N, i.e. x times
+ * the transposed dequantized weight matrix ([MC] CUDA: the matmul consumes
+ * packed codes plus group scales).  Naive loops over m, n, then k. */
+int oracle_matmul(const void *x, int xdt, int64_t M, int64_t K,
+                  const uint32_t *codes, const uint16_t *scales, int64_t N,
+                  double *y, double *bound)
+{
+    int rc = 0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            rc |= one_output(x, xdt, K, codes, scales, m, n,
+                             &y[m * N + n], &bound[m * N + n]);
+    return rc;
+}
+
+/* The same definition at a list of (m, n) output positions only. */
+int oracle_matmul_at(const void *x, int xdt, int64_t K,
+                     const uint32_t *codes, const uint16_t *scales,
+                     const int64_t *ms, const int64_t *ns, int64_t count,
+                     double *y, double *bound)
+{
+    int rc = 0;
+    for (int64_t i = 0; i < count; ++i)
+        rc |= one_output(x, xdt, K, codes, scales, ms[i], ns[i], &y[i], &bound[i]);
+    return rc;
+}
+
+/* popcount of a 64-bit value, bit by bit. */
+static int popcount64(uint64_t v)
+{
+    int c = 0;
+    while (v) { c += (int)(v & 1u); v >>= 1; }
+    return c;
+}
+
+/* Entry (i, l) of the b x b Sylvester Hadamard matrix: (-1)^popcount(i & l). */
+double oracle_hadamard_entry(int64_t i, int64_t l)
+{
+    return (popcount64((uint64_t)(i & l)) & 1) ? -1.0 : 1.0;
+}
+
+/* Signed normalized Walsh-Hadamard transform along the last dimension, in
+ * contiguous blocks of b ([9B] section 3: normalized Sylvester-Walsh-Hadamard,
+ * block 4096, last dimension, explicit sign pattern).
+ *   forward:  y = (1/sqrt(b)) H_b (d .* x)     (per block)
+ *   inverse:  y = d .* ((1/sqrt(b)) H_b x)     (per block)
+ * d is the +-1 sign vector of length K (NULL means all +1).  The matrix is
+ * applied entry by entry, O(b^2) per block.  Returns 1 if K % b != 0. */
+int oracle_fwht(const double *x, const int8_t *signs, int64_t M, int64_t K,
+                int64_t b, int inverse, double *y)
+{
+    if (b <= 0 || K % b != 0) return 1;
+    double norm = 1.0 / sqrt((double)b);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; j += b)
+            for (int64_t i = 0; i < b; ++i) {
+                double acc = 0.0;
+                for (int64_t l = 0; l < b; ++l) {
+                    double v = x[m * K + j + l];
+                    if (!inverse && signs) v *= (double)signs[j + l];
+                    acc += oracle_hadamard_entry(i, l) * v;
+                }
+                acc *= norm;
+                if (inverse && signs) acc *= (double)signs[j + i];
+                y[m * K + j + i] = acc;
+            }
+    return 0;
+}
+
+/* Lossless reading of an FP32 matrix as ternary-g128 ([9B] section 3: the
+ * transcode to 2-bit groups of 128 is lossless).  A group is ternary iff all
+ * its nonzero |w| equal one value a that binary16 represents exactly; then
+ * s = a (s = +0 for an all-zero group) and t = sign(w).  Returns 0, or 2 at
+ * the first group that is not of that form.  scale_bits receives the
+ * binary16 bit pattern of s. */
+int oracle_ternary_from_f32(const float *w, int64_t N, int64_t K,
+                            int8_t *t, uint16_t *scale_bits)
+{
+    int64_t G = K / ORACLE_GROUP;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < G; ++g) {
+            double a = 0.0;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k) {
+                double v = fabs((double)w[n * K + k]);
+                if (v == 0.0) continue;
+                if (!isfinite(v)) return 2;
+                if (a == 0.0) a = v;
+                else if (v != a) return 2;
+            }
+            /* find the binary16 pattern whose value is exactly a */
+            uint16_t bits = 0;
+            int found = (a == 0.0);
+            for (uint32_t h = 0; h < 0x7c00u && !found; ++h)
+                if (oracle_half_to_double((uint16_t)h) == a) { bits = (uint16_t)h; found = 1; }
+            if (!found) return 2;
+            scale_bits[n * G + g] = bits;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k) {
+                float v = w[n * K + k];
+                t[n * K + k] = (int8_t)((v > 0.0f) - (v < 0.0f));
+            }
+        }
+    return 0;
+}
+
+/* Storage accounting of the 2-bit-slot format ([MC] Memory requirement):
+ * N*K/4 bytes of codes plus 2 bytes of FP16 scale per 128 weights. */
+double oracle_bits_per_weight(int64_t N, int64_t K)
+{
+    double code_bytes = (double)N * (double)K / 4.0;
+    double scale_bytes = 2.0 * (double)N * (double)K / ORACLE_GROUP;
+    return 8.0 * (code_bytes + scale_bytes) / ((double)N * (double)K);
+}
