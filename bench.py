@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary-g128 decode hot path on one MI355X.
+
+One step = the rotated decode path for one token: sign flip + signed
+normalized Walsh-Hadamard transform (block 4096) of a bfloat16 activation
+row, then the ternary-g128 GEMV M=1, K=4096 -> N=12288 on the rotated
+binary32 activations.  Inputs are seeded synthetic arrays resident in HBM
+before timing starts.  Weights rotate over a pool of distinct copies larger
+than 1 GiB so that neither L2 nor the 256 MB MALL can serve repeats, and the
+K timed steps are captured in one HIP graph (host launch overhead would
+otherwise dominate microsecond kernels).
+
+Prints one JSON line.  `value` is algorithmic bytes per step / step time.
+`roofline` covers the dominant kernel (the GEMV), timed with HIP events on
+the stream it runs on.  `cpu_baseline` is the FP64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+POOL_BYTES = 1 << 30           # rotate weights over at least this much HBM
+METRIC = "ternary GEMV HBM GB/s (M=1) & % of peak; pp512 GEMM TFLOP/s & % MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="rotated",
+                   choices=["rotated", "sweep", "prefill", "all"],
+                   help="rotated: the headline step; sweep / prefill: extra measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-secondary", action="store_true", help="headline line only")
+    return p.parse_args()
+
+
+def gemv_bytes(M, K, N, x_bytes):
+    return N * K // 4 + 2 * N * K // 128 + M * K * x_bytes + M * N * 4
+
+
+def make_pool(tern, torch, t, s, nbytes_each):
+    codes, s2 = tern.tern_pack(t, s)
+    c0, s0 = tern.to_device(codes, s2)
+    copies = max(2, -(-POOL_BYTES // nbytes_each))
+    pool = [(c0, s0)] + [(c0.clone(), s0.clone()) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    return pool
+
+
+def time_graph(torch, fn, steps):
+    """Capture `steps` calls of fn(i) in one HIP graph, replay once, return
+    elapsed ms from HIP events recorded on the replay stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()                       # upload / first replay, untimed
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start.record(cur)
+    g.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), g
+
+
+def rotated_step_setup(tern, torch, synth):
+    w = synth.ROTATED
+    seed = 11
+    t = synth.ternary(seed, w.N, w.K, w.p_zero)
+    s = synth.scales_f16(seed, w.N, w.K)
+    x = synth.activations_bf16(seed, w.M, w.K)
+    d = synth.signs(seed, w.K)
+    wbytes = tern.tern_codes_bytes(w.N, w.K) + tern.tern_scales_bytes(w.N, w.K)
+    pool = make_pool(tern, torch, t, s, wbytes)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    dd = torch.from_numpy(d).cuda()
+    xr = torch.empty((w.M, w.K), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    return w, (t, s, x, d), pool, xd, dd, xr, y
+
+
+def bench_rotated(args, tern, torch, synth):
+    w, host, pool, xd, dd, xr, y = rotated_step_setup(tern, torch, synth)
+    P = len(pool)
+
+    def step(i):
+        c, s = pool[i % P]
+        tern.tern_fwht(xd, dd, w.rotate_block, out=xr)
+        tern.tern_gemv(xr, c, s, out=y)
+
+    def gemv_only(i):
+        c, s = pool[i % P]
+        tern.tern_gemv(xr, c, s, out=y)
+
+    def fwht_only(i):
+        tern.tern_fwht(xd, dd, w.rotate_block, out=xr)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # the timed region: exactly `steps` steps, synchronized on both sides
+    torch.cuda.synchronize()
+    step_ms, g = time_graph(torch, step, args.steps)
+    ms_per_step = step_ms / args.steps
+    gemv_ms, _ = time_graph(torch, gemv_only, args.steps)
+    fwht_ms, _ = time_graph(torch, fwht_only, args.steps)
+    gemv_us = 1e3 * gemv_ms / args.steps
+    fwht_us = 1e3 * fwht_ms / args.steps
+
+    # sanity: a replay of the timed graph reproduces the eager result
+    step(args.steps - 1)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_eager), "graph replay differs from eager execution"
+
+    gb = gemv_bytes(w.M, w.K, w.N, 4)
+    fwht_b = w.M * w.K * 2 + w.K + w.M * w.K * 4
+    step_bytes = gb + fwht_b
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = gb / (gemv_us * 1e-6) / 1e9
+    res = {
+        "value": value,
+        "ms_per_step": ms_per_step,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "detail": {"gemv_us": gemv_us, "fwht_us": fwht_us, "gemv_bytes": gb, "step_bytes": step_bytes,
+                   "pool_copies": P, "pool_bytes": P * (tern.tern_codes_bytes(w.N, w.K) +
+                                                        tern.tern_scales_bytes(w.N, w.K))},
+    }
+    return w, host, res
+
+
+def cpu_baseline(w, host, min_seconds=10.0):
+    """The FP64 oracle, as it stands, on the same step: explicit-matrix
+    rotation then the naive matmul over all rows, single thread."""
+    import oracle
+    t, s, x, d = host
+    codes = oracle.encode(t)
+    x64 = oracle.bf16_bits_to_f64(x)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        xr = oracle.fwht(x64, d, w.rotate_block)
+        oracle.matmul(xr, codes, s, w.K)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    step_bytes = gemv_bytes(w.M, w.K, w.N, 4) + w.M * w.K * 2 + w.K + w.M * w.K * 4
+    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full rotated decode steps (FP64 explicit-Hadamard rotation + "
+                      f"naive FP64 matmul over all {w.N} rows), {el:.1f} s, single thread"}
+
+
+def bench_sweep(tern, torch, synth, steps):
+    """Decode GEMV at M = 1, 16 on both MLP shapes, rotated pool, graph-timed."""
+    out = {}
+    for (K, N) in ((5120, 17408), (17408, 5120)):
+        seed = 5 + K
+        t = synth.ternary(seed, N, K)
+        s = synth.scales_f16(seed, N, K)
+        pool = make_pool(tern, torch, t, s, tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K))
+        P = len(pool)
+        for M in (1, 2, 4, 8, 16):
+            x = synth.activations_bf16(seed, M, K)
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+            def fn(i, xd=xd, y=y):
+                c, s_ = pool[i % P]
+                tern.tern_gemv(xd, c, s_, out=y)
+
+            for i in range(5):
+                fn(i)
+            ms, _ = time_graph(torch, fn, steps)
+            us = 1e3 * ms / steps
+            gbs = gemv_bytes(M, K, N, 2) / (us * 1e-6) / 1e9
+            out[f"M{M}_K{K}_N{N}"] = {"us": us, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_prefill(tern, torch, synth, steps):
+    out = {}
+    for w in synth.PREFILL:
+        seed = 9 + w.K
+        t = synth.ternary(seed, w.N, w.K, w.p_zero)
+        s = synth.scales_f16(seed, w.N, w.K)
+        codes, s2 = tern.tern_pack(t, s)
+        c, sd = tern.to_device(codes, s2)
+        x = synth.activations_bf16(seed, w.M, w.K, w.outlier_frac)
+        xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        ws_n = tern.tern_gemm_workspace_bytes(w.M, w.N, w.K)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            tern.tern_gemm(xd, c, sd, out=y, workspace=ws)
+
+        for i in range(3):
+            fn(i)
+        ms, _ = time_graph(torch, fn, steps)
+        us = 1e3 * ms / steps
+        tf = 2.0 * w.M * w.N * w.K / (us * 1e-6) / 1e12
+        out[f"M{w.M}_K{w.K}_N{w.N}"] = {"us": us, "TFLOP/s": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; the kernels are single-GPU "
+                                   "and --gpus above 1 is not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    import ternary_weight_g128_amd as tern
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.workload in ("sweep", "prefill"):
+        fn = bench_sweep if args.workload == "sweep" else bench_prefill
+        print(json.dumps({args.workload: fn(tern, torch, synth, args.steps)}))
+        return
+
+    w, host, res = bench_rotated(args, tern, torch, synth)
+    line = {
+        "metric": METRIC,
+        "value": res["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "rotated decode: sign flip + normalized Walsh-Hadamard (block 4096) "
+                               "+ ternary-g128 GEMV M=1 K=4096 N=12288",
+                   "M": w.M, "K": w.K, "N": w.N, "graph_captured": True,
+                   "weight_pool_bytes": res["detail"]["pool_bytes"]},
+        "roofline": res["roofline"],
+        "detail": res["detail"],
+    }
+    if not args.no_secondary:
+        line["secondary"] = {
+            "decode_sweep_gemv": bench_sweep(tern, torch, synth, 200),
+            "prefill_gemm": bench_prefill(tern, torch, synth, 20),
+        }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, host)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * tern.h -- C ABI of libtern: ternary-g128 weights on AMD MI355X (gfx950).
+ *
+ * The weight format ("prism-ml/Ternary-Bonsai-27B-mlx-2bit" model card,
+ * sections "Weight representation: ternary g128" and "Memory requirement"):
+ * every weight is t in {-1, 0, +1}; each run of 128 consecutive weights along
+ * K in one output row shares one IEEE binary16 scale s_g, so the weight value
+ * is w = s_g * t; each t is stored in a 2-bit slot, 2.125 bits per weight.
+ *
+ * The matmul ("CUDA (NVIDIA GPUs)" section of the same card) unpacks the
+ * codes and applies the group scales inside the kernel; the weights are never
+ * expanded to a dense FP16 tensor in memory.
+ *
+ * The optional activation rotation ("Ternary-Bonsai-2-9B-2bit" article,
+ * section 3, "Ternary weights and Hadamard rotation") is a normalized
+ * Sylvester-Walsh-Hadamard transform with an explicit +-1 sign pattern over
+ * blocks of the last dimension (block 4096 in that model); the rotation is
+ * folded into the stored weights and the matching transform is applied to
+ * activations at run time, forward and inverse.
+ *
+ * Layouts (all row-major, K contiguous):
+ *   x      [M][K]      activations, binary32 or bfloat16
+ *   codes  [N][K/16]   uint32; slot j of word w of row n holds
+ *                      q = t[n][16w + j] + 1 at bits 2j..2j+1 (q = 3 unused)
+ *   scales [N][K/128]  binary16 bit patterns
+ *   y      [M][N]      binary32 (or bfloat16 where stated)
+ *
+ * Conventions for every call:
+ *   - The caller owns and allocates every buffer; the library allocates
+ *     nothing.  Host-codec calls take host pointers and are synchronous.
+ *     Device calls take device pointers on the current HIP device and are
+ *     enqueued on `stream` (a hipStream_t; NULL is the null stream); they
+ *     return once the work is enqueued.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns a status and launches nothing.  tern_last_error()
+ *     then holds a one-line reason (thread-local).  No exception crosses the
+ *     ABI.  A HIP launch failure returns TERN_EDEVICE with the HIP message.
+ *   - M, N, K are >= 0; a zero M or N writes nothing; K = 0 writes zeros
+ *     (an empty sum).  K must be a multiple of 128 (whole scale groups).
+ *   - Device kernels do not check code values: a slot holding 3 gives an
+ *     unspecified result (it is never produced by the packer).
+ *   - Results are bitwise reproducible run to run for the same arguments.
+ *   - Calls are stateless and may be made from several host threads.
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tern_status {
+    TERN_OK = 0,
+    TERN_EINVAL = 1,        /* bad size, pointer, alignment or non-finite scale */
+    TERN_ENOTTERNARY = 2,   /* input values are not ternary-g128 */
+    TERN_EBADCODE = 3,      /* a 2-bit slot holds the unused value 3 */
+    TERN_EUNSUPPORTED = 4,  /* valid request this build does not implement */
+    TERN_EDEVICE = 5        /* HIP runtime error */
+} tern_status;
+
+typedef enum tern_dtype {
+    TERN_F32 = 0,           /* IEEE binary32 */
+    TERN_BF16 = 1           /* bfloat16 (upper half of binary32) */
+} tern_dtype;
+
+#define TERN_GROUP 128            /* weights per FP16 scale */
+#define TERN_SLOTS_PER_WORD 16    /* 2-bit slots per uint32 code word */
+#define TERN_GEMV_MAX_M 16        /* rows of x one tern_gemv call takes */
+#define TERN_FWHT_MAX_BLOCK 4096  /* largest Hadamard block tern_fwht takes */
+#define TERN_ABI_VERSION 1
+
+/* ABI version of the loaded library (TERN_ABI_VERSION it was built with). */
+int tern_abi_version(void);
+
+/* Static name of a status code ("TERN_OK", ...); "unknown" otherwise. */
+const char *tern_status_str(int status);
+
+/* Reason for the last non-OK status returned on this host thread, or "". */
+const char *tern_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Storage accounting ("Memory requirement": 2-bit slots + one FP16 scale per
+ * 128 weights = 2.125 bits/weight).  Pure functions; 0 for invalid sizes
+ * (negative, or K not a multiple of 128).
+ * ------------------------------------------------------------------------ */
+size_t tern_codes_bytes(int64_t N, int64_t K);   /* N*K/4  */
+size_t tern_scales_bytes(int64_t N, int64_t K);  /* 2*N*K/128 */
+
+/* ---------------------------------------------------------------------------
+ * Host codec (lossless transcode into the 2-bit g128 slot format; the
+ * "Ternary-Bonsai-2-9B-2bit" article, section 3, describes the transcode as
+ * lossless).  Host pointers, caller-owned, synchronous.
+ * ------------------------------------------------------------------------ */
+
+/* Pack t[N][K] (int8, each -1, 0 or +1) into codes[N][K/16] and copy the
+ * binary16 scales s_f16[N][K/128] to s_out (s_out may equal s_f16).
+ * Errors: TERN_EINVAL (sizes, NULL, K % 128, a non-finite scale),
+ * TERN_ENOTTERNARY (some t outside {-1,0,1}; codes then undefined). */
+tern_status tern_pack(const int8_t *t, const uint16_t *s_f16, int64_t N, int64_t K,
+                      uint32_t *codes, uint16_t *s_out);
+
+/* Lossless reading of FP32 weights w[N][K] as ternary-g128: a group is
+ * accepted iff all its nonzero |w| equal one value a that binary16
+ * represents exactly; then s = a (+0 for an all-zero group) and t = sign(w).
+ * This is not a quantizer: any other group gives TERN_ENOTTERNARY.
+ * Outputs codes[N][K/16] and s_out[N][K/128]. */
+tern_status tern_pack_f32(const float *w, int64_t N, int64_t K,
+                          uint32_t *codes, uint16_t *s_out);
+
+/* Decode codes[N][K/16] into t[N][K] (int8).  TERN_EBADCODE if a slot holds 3. */
+tern_status tern_unpack(const uint32_t *codes, int64_t N, int64_t K, int8_t *t);
+
+/* Dense w[N][K] = s_g * t in binary32 (exact).  TERN_EBADCODE on slot 3. */
+tern_status tern_dequant_f32(const uint32_t *codes, const uint16_t *s_f16,
+                             int64_t N, int64_t K, float *w);
+
+/* ---------------------------------------------------------------------------
+ * Device operations.  Device pointers; enqueued on `stream`.
+ * ------------------------------------------------------------------------ */
+
+/* Signed normalized Walsh-Hadamard transform along the last dimension, over
+ * contiguous blocks of `block` elements ("Ternary-Bonsai-2-9B-2bit",
+ * section 3), in natural Sylvester order H[i][l] = (-1)^popcount(i & l):
+ *   inverse == 0:  y[m, jb+i] = b^-1/2 sum_l H[i][l] d[jb+l] x[m, jb+l]
+ *   inverse != 0:  y[m, jb+i] = d[jb+i] b^-1/2 sum_l H[i][l] x[m, jb+l]
+ * x: [M][K] TERN_F32 or TERN_BF16; signs: int8 [K] of +-1, or NULL for all +1
+ * (other values are multiplied in as given); y: float [M][K], which may be
+ * the same buffer as x when xdt == TERN_F32.  block: a power of two in
+ * [1, 4096]; K % block == 0.  x and y 16-byte aligned.
+ * Accuracy: within 1e-5 relative L2 error per row of the exact transform.
+ * Errors: TERN_EINVAL, TERN_EUNSUPPORTED (dtype), TERN_EDEVICE. */
+tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, int64_t K,
+                      int64_t block, int inverse, float *y, void *stream);
+
+/* Decode-regime matmul y[m][n] = sum_k s_g t[n][k] x[m][k] for M <= 16
+ * ("CUDA (NVIDIA GPUs)": fused unpack + group scale).  The codes are streamed
+ * once from HBM; products are formed exactly and accumulated in binary32
+ * per 128-K group, then scaled.
+ * x: [M][K], xdt TERN_F32 or TERN_BF16, 16-byte aligned; codes [N][K/16]
+ * 16-byte aligned; scales [N][K/128] 2-byte aligned; y [M][N] written as
+ * ydt (TERN_F32, or TERN_BF16 rounded to nearest even), aligned to its dtype.
+ * Accuracy: |y - exact| <= 1e-4 * sum_k |s_g t x_k| per element (binary32
+ * output; a bfloat16 output adds its own rounding).
+ * Errors: TERN_EINVAL (M > 16, sizes, alignment, NULL), TERN_EUNSUPPORTED
+ * (dtype), TERN_EDEVICE. */
+tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K,
+                      const uint32_t *codes, const uint16_t *scales, int64_t N,
+                      void *y, int ydt, void *stream);
+
+/* Bytes of device workspace tern_gemm needs for these sizes (may be 0). */
+size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Prefill-regime matmul, same definition as tern_gemv, any M >= 0 (tuned for
+ * M >= 64): unpacked codes feed bf16 matrix-core (MFMA) tiles; accumulation
+ * is binary32 per 128-K group, then scaled by s_g in binary32.
+ * x: [M][K] TERN_BF16 only, 16-byte aligned; codes 16-byte aligned;
+ * y: float [M][N]; workspace: device memory of at least
+ * tern_gemm_workspace_bytes(M, N, K) bytes (NULL allowed when that is 0).
+ * Accuracy as tern_gemv.  Errors: TERN_EINVAL, TERN_EUNSUPPORTED,
+ * TERN_EDEVICE. */
+tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K,
+                      const uint32_t *codes, const uint16_t *scales, int64_t N,
+                      float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

@@ -27,15 +27,30 @@ def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
 
 
-def ternary(seed: int, N: int, K: int, p_zero: float = 1.0 / 3.0) -> np.ndarray:
-    """int8 [N, K], i.i.d. with P(0) = p_zero and P(+1) = P(-1) = (1-p_zero)/2."""
-    r = _rng(seed, _S_T)
-    u = r.random((N, K))
+def _ternary_from_uniform(u: np.ndarray, p_zero: float) -> np.ndarray:
     half = (1.0 - p_zero) / 2.0
-    t = np.zeros((N, K), dtype=np.int8)
+    t = np.zeros(u.shape, dtype=np.int8)
     t[u < half] = -1
     t[u >= half + p_zero] = 1
     return t
+
+
+def ternary(seed: int, N: int, K: int, p_zero: float = 1.0 / 3.0) -> np.ndarray:
+    """int8 [N, K], i.i.d. with P(0) = p_zero and P(+1) = P(-1) = (1-p_zero)/2."""
+    return np.concatenate(list(ternary_chunks(seed, N, K, p_zero)), axis=0) if N else \
+        np.zeros((0, K), dtype=np.int8)
+
+
+def ternary_chunks(seed: int, N: int, K: int, p_zero: float = 1.0 / 3.0,
+                   max_elems: int = 1 << 23):
+    """The rows of ternary(seed, N, K, p_zero), yielded in consecutive row
+    chunks of at most max_elems elements (the same stream, drawn in order),
+    so large matrices never exist in float64 on the host."""
+    r = _rng(seed, _S_T)
+    rows = max(1, max_elems // max(K, 1))
+    for n0 in range(0, N, rows):
+        nr = min(rows, N - n0)
+        yield _ternary_from_uniform(r.random((nr, K)), p_zero)
 
 
 def scales_f16(seed: int, N: int, K: int, sigma: float = 0.02, floor: float = 1e-3) -> np.ndarray:

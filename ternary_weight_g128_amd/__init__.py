@@ -1,0 +1,238 @@
+"""Python binding of libtern (ternary-g128 matmul and signed Walsh-Hadamard
+rotation for AMD MI355X).
+
+Argument marshalling only: every computation runs in libtern.so (host codec
+in C++, device operations in HIP kernels).  Host-codec functions take numpy
+arrays; device functions take torch tensors on the current HIP device and
+enqueue on torch's current stream.  The names are the C ABI names of
+include/tern.h.  A missing or unloadable libtern.so raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtern.so")
+
+TERN_OK, TERN_EINVAL, TERN_ENOTTERNARY, TERN_EBADCODE, TERN_EUNSUPPORTED, TERN_EDEVICE = range(6)
+TERN_F32, TERN_BF16 = 0, 1
+TERN_GROUP = 128
+TERN_GEMV_MAX_M = 16
+TERN_FWHT_MAX_BLOCK = 4096
+
+EXPORTED = [
+    "tern_abi_version", "tern_status_str", "tern_last_error", "tern_codes_bytes",
+    "tern_scales_bytes", "tern_pack", "tern_pack_f32", "tern_unpack", "tern_dequant_f32",
+    "tern_fwht", "tern_gemv", "tern_gemm_workspace_bytes", "tern_gemm",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libtern.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_lib.tern_abi_version.restype = _I
+_lib.tern_status_str.argtypes = [_I]
+_lib.tern_status_str.restype = ctypes.c_char_p
+_lib.tern_last_error.restype = ctypes.c_char_p
+_lib.tern_codes_bytes.argtypes = [_I64, _I64]
+_lib.tern_codes_bytes.restype = _SZ
+_lib.tern_scales_bytes.argtypes = [_I64, _I64]
+_lib.tern_scales_bytes.restype = _SZ
+_lib.tern_pack.argtypes = [_P, _P, _I64, _I64, _P, _P]
+_lib.tern_pack_f32.argtypes = [_P, _I64, _I64, _P, _P]
+_lib.tern_unpack.argtypes = [_P, _I64, _I64, _P]
+_lib.tern_dequant_f32.argtypes = [_P, _P, _I64, _I64, _P]
+_lib.tern_fwht.argtypes = [_P, _I, _P, _I64, _I64, _I64, _I, _P, _P]
+_lib.tern_gemv.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
+_lib.tern_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
+_lib.tern_gemm_workspace_bytes.restype = _SZ
+_lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
+for _name in EXPORTED:
+    if _name not in ("tern_abi_version", "tern_status_str", "tern_last_error",
+                     "tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes"):
+        getattr(_lib, _name).restype = _I
+
+
+class TernError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.tern_last_error().decode()
+        super().__init__(f"{where}: {_lib.tern_status_str(status).decode()}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != TERN_OK:
+        raise TernError(status, where)
+
+
+def lib():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def tern_abi_version() -> int:
+    return _lib.tern_abi_version()
+
+
+def tern_status_str(status: int) -> str:
+    return _lib.tern_status_str(status).decode()
+
+
+def tern_last_error() -> str:
+    return _lib.tern_last_error().decode()
+
+
+def tern_codes_bytes(N: int, K: int) -> int:
+    return _lib.tern_codes_bytes(N, K)
+
+
+def tern_scales_bytes(N: int, K: int) -> int:
+    return _lib.tern_scales_bytes(N, K)
+
+
+# --------------------------------------------------------------------------
+# host codec (numpy in, numpy out)
+# --------------------------------------------------------------------------
+
+def _np_ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def tern_pack(t: np.ndarray, s_f16: np.ndarray):
+    """t int8 [N, K], binary16 scale bits uint16 [N, K/128] ->
+    (codes uint32 [N, K/16], scales uint16 [N, K/128])."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    N, K = t.shape
+    s = np.ascontiguousarray(s_f16, dtype=np.uint16)
+    if K % TERN_GROUP or s.shape != (N, K // TERN_GROUP):
+        raise ValueError("tern_pack: need K % 128 == 0 and scales of shape [N, K/128]")
+    codes = np.empty((N, K // 16), dtype=np.uint32)
+    s_out = np.empty_like(s)
+    _check(_lib.tern_pack(_np_ptr(t), _np_ptr(s), N, K, _np_ptr(codes), _np_ptr(s_out)), "tern_pack")
+    return codes, s_out
+
+
+def tern_pack_f32(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % TERN_GROUP:
+        raise ValueError("tern_pack_f32: K % 128 != 0")
+    codes = np.empty((N, K // 16), dtype=np.uint32)
+    s = np.empty((N, K // TERN_GROUP), dtype=np.uint16)
+    _check(_lib.tern_pack_f32(_np_ptr(w), N, K, _np_ptr(codes), _np_ptr(s)), "tern_pack_f32")
+    return codes, s
+
+
+def tern_unpack(codes: np.ndarray, K: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    N = codes.shape[0]
+    t = np.empty((N, K), dtype=np.int8)
+    _check(_lib.tern_unpack(_np_ptr(codes), N, K, _np_ptr(t)), "tern_unpack")
+    return t
+
+
+def tern_dequant_f32(codes: np.ndarray, s_f16: np.ndarray, K: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    s = np.ascontiguousarray(s_f16, dtype=np.uint16)
+    N = codes.shape[0]
+    w = np.empty((N, K), dtype=np.float32)
+    _check(_lib.tern_dequant_f32(_np_ptr(codes), _np_ptr(s), N, K, _np_ptr(w)), "tern_dequant_f32")
+    return w
+
+
+# --------------------------------------------------------------------------
+# device operations (torch tensors on the current HIP device)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TERN_F32
+    if t.dtype == torch.bfloat16:
+        return TERN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device operations take tensors on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def tern_fwht(x, signs, block: int, inverse: bool = False, out=None, stream=None):
+    """Signed normalized Walsh-Hadamard transform along the last dim.
+    x: [M, K] float32 or bfloat16; signs: int8 [K] or None; returns float32
+    [M, K] (out may be x itself when x is float32)."""
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _check(_lib.tern_fwht(_dev_ptr(x), _dt(x), _dev_ptr(signs), M, K, block, int(bool(inverse)),
+                          _dev_ptr(out), _stream_ptr(stream)), "tern_fwht")
+    return out
+
+
+def tern_gemv(x, codes, scales, out=None, out_dtype=None, stream=None):
+    """y[M, N] = x[M, K] (s_g t)^T for M <= 16.  codes int32 [N, K/16] (bit
+    patterns of the uint32 words), scales int16 [N, K/128] (binary16 bits)."""
+    torch = _torch()
+    M, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    _check(_lib.tern_gemv(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
+                          _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv")
+    return out
+
+
+def tern_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return _lib.tern_gemm_workspace_bytes(M, N, K)
+
+
+def tern_gemm(x, codes, scales, out=None, workspace=None, stream=None):
+    """y[M, N] = x[M, K] (s_g t)^T, bfloat16 x, any M."""
+    torch = _torch()
+    M, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = tern_gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.tern_gemm(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
+                          _dev_ptr(out), _dev_ptr(workspace), ws_bytes, _stream_ptr(stream)),
+           "tern_gemm")
+    return out
+
+
+def to_device(codes: np.ndarray, scales: np.ndarray, device="cuda"):
+    """Upload packed weights as int32 / int16 tensors (same bits)."""
+    torch = _torch()
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint32).view(np.int32)).to(device)
+    s = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint16).view(np.int16)).to(device)
+    return c, s

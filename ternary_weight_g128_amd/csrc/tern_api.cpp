@@ -1,0 +1,162 @@
+// C ABI of libtern: argument validation on the host, then kernel launch on
+// the caller's stream.  Nothing here allocates device memory.
+#include <cstdint>
+#include <string>
+
+#include "tern_internal.h"
+
+using tern::set_error;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tern_status device_status(int err, const char *what)
+{
+    if (err == 0) return TERN_OK;
+    set_error(std::string(what) + ": HIP error " + std::to_string(err) + " (" +
+              tern::hip_error_string(err) + ")");
+    return TERN_EDEVICE;
+}
+
+tern_status check_matmul_args(const char *fn, const void *x, int xdt, int64_t M, int64_t K,
+                              const uint32_t *codes, const uint16_t *scales, int64_t N,
+                              const void *y)
+{
+    if (M < 0 || N < 0 || K < 0) {
+        set_error(std::string(fn) + ": negative size");
+        return TERN_EINVAL;
+    }
+    if (K % TERN_GROUP != 0) {
+        set_error(std::string(fn) + ": K must be a multiple of 128 (whole scale groups)");
+        return TERN_EINVAL;
+    }
+    if (xdt != TERN_F32 && xdt != TERN_BF16) {
+        set_error(std::string(fn) + ": activation dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (!y || (K > 0 && (!x || !codes || !scales))) {
+        set_error(std::string(fn) + ": NULL pointer");
+        return TERN_EINVAL;
+    }
+    if (K > 0 && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2))) {
+        set_error(std::string(fn) + ": x and codes must be 16-byte aligned, scales 2-byte aligned");
+        return TERN_EINVAL;
+    }
+    if ((int64_t)N * (K / 16) >= ((int64_t)1 << 40)) {
+        set_error(std::string(fn) + ": matrix too large");
+        return TERN_EINVAL;
+    }
+    return TERN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *codes,
+                      const uint16_t *scales, int64_t N, void *y, int ydt, void *stream)
+{
+    tern_status st = check_matmul_args("tern_gemv", x, xdt, M, K, codes, scales, N, y);
+    if (st != TERN_OK) return st;
+    if (M > TERN_GEMV_MAX_M) {
+        set_error("tern_gemv: M must be at most 16 (use tern_gemm for larger M)");
+        return TERN_EINVAL;
+    }
+    if (ydt != TERN_F32 && ydt != TERN_BF16) {
+        set_error("tern_gemv: output dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (!aligned(y, ydt == TERN_F32 ? 4 : 2)) {
+        set_error("tern_gemv: y not aligned to its dtype");
+        return TERN_EINVAL;
+    }
+    if (N > ((int64_t)1 << 31) - 64) {
+        set_error("tern_gemv: N too large");
+        return TERN_EINVAL;
+    }
+    return device_status(tern::launch_gemv(x, xdt == TERN_F32, (int)M, K, codes, scales, N, y,
+                                           ydt == TERN_BF16, stream),
+                         "tern_gemv");
+}
+
+size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || K % TERN_GROUP) return 0;
+    return tern::gemm_workspace_bytes(M, N, K);
+}
+
+tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *codes,
+                      const uint16_t *scales, int64_t N, float *y, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    tern_status st = check_matmul_args("tern_gemm", x, xdt, M, K, codes, scales, N, y);
+    if (st != TERN_OK) return st;
+    if (xdt != TERN_BF16) {
+        set_error("tern_gemm: activations must be TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (!aligned(y, 4)) {
+        set_error("tern_gemm: y must be 4-byte aligned");
+        return TERN_EINVAL;
+    }
+    if (M > ((int64_t)1 << 31) - 256 || N > ((int64_t)1 << 31) - 256) {
+        set_error("tern_gemm: M or N too large");
+        return TERN_EINVAL;
+    }
+    const size_t need = tern::gemm_workspace_bytes(M, N, K);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))) {
+        set_error("tern_gemm: workspace missing, misaligned or smaller than "
+                  "tern_gemm_workspace_bytes() = " + std::to_string(need));
+        return TERN_EINVAL;
+    }
+    return device_status(
+        tern::launch_gemm(x, M, K, codes, scales, N, y, workspace, workspace_bytes, stream),
+        "tern_gemm");
+}
+
+tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, int64_t K,
+                      int64_t block, int inverse, float *y, void *stream)
+{
+    if (M < 0 || K < 0) {
+        set_error("tern_fwht: negative size");
+        return TERN_EINVAL;
+    }
+    if (block < 1 || block > TERN_FWHT_MAX_BLOCK || (block & (block - 1)) != 0) {
+        set_error("tern_fwht: block must be a power of two in [1, 4096]");
+        return TERN_EINVAL;
+    }
+    if (K % block != 0) {
+        set_error("tern_fwht: K must be a multiple of block");
+        return TERN_EINVAL;
+    }
+    if (xdt != TERN_F32 && xdt != TERN_BF16) {
+        set_error("tern_fwht: activation dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || K == 0) return TERN_OK;
+    if (!x || !y) {
+        set_error("tern_fwht: NULL pointer");
+        return TERN_EINVAL;
+    }
+    if (!aligned(x, 16) || !aligned(y, 16)) {
+        set_error("tern_fwht: x and y must be 16-byte aligned");
+        return TERN_EINVAL;
+    }
+    if (xdt == TERN_BF16 && static_cast<const void *>(y) == x) {
+        set_error("tern_fwht: in-place operation needs TERN_F32 activations");
+        return TERN_EINVAL;
+    }
+    if (K / block > ((int64_t)1 << 31) - 1) {
+        set_error("tern_fwht: too many blocks for one launch");
+        return TERN_EINVAL;
+    }
+    return device_status(tern::launch_fwht(x, xdt == TERN_F32, signs, M, K, (int)block,
+                                           inverse != 0, y, stream),
+                         "tern_fwht");
+}
+
+}  // extern "C"

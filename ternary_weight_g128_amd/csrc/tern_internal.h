@@ -1,0 +1,30 @@
+// Internal declarations shared by the libtern translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "tern.h"
+
+namespace tern {
+
+// Thread-local reason for the last failing call.
+void set_error(const std::string &msg);
+void clear_error();
+
+// Kernel launchers (tern_kernels.hip).  Arguments are already validated.
+// They return hipSuccess or the launch error code (as int, to keep HIP types
+// out of this header).
+int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *codes,
+                const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream);
+int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64_t K,
+                int block, bool inverse, float *y, void *stream);
+int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes,
+                const uint16_t *scales, int64_t N, float *y, void *workspace,
+                size_t workspace_bytes, void *stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+const char *hip_error_string(int err);
+
+}  // namespace tern

@@ -1,0 +1,137 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/tern.h declares, and rejects bad arguments on the host with
+the documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tern():
+    import ternary_weight_g128_amd as t
+    return t
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tern.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tern_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ["tern_pack", "tern_fwht", "tern_gemv", "tern_gemm"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_function(tern):
+    lib = ctypes.CDLL(tern.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(tern.EXPORTED) == _declared_functions()
+
+
+def test_abi_version_and_status_strings(tern):
+    assert tern.tern_abi_version() == 1
+    assert tern.tern_status_str(0) == "TERN_OK"
+    assert tern.tern_status_str(5) == "TERN_EDEVICE"
+    assert tern.tern_status_str(99) == "unknown"
+
+
+def test_accounting_functions(tern):
+    assert tern.tern_codes_bytes(17408, 5120) == 17408 * 5120 // 4
+    assert tern.tern_scales_bytes(17408, 5120) == 2 * 17408 * 5120 // 128
+    for N, K in [(1, 128), (1024, 1024), (12288, 4096)]:
+        b = tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K)
+        assert 8 * b / (N * K) == 2.125
+    assert tern.tern_codes_bytes(4, 100) == 0 and tern.tern_scales_bytes(-1, 128) == 0
+
+
+# Fake, never-dereferenced device addresses: validation must fail before any
+# HIP call, so these calls are safe without a GPU.
+A16 = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x10002)
+NULL = None
+
+
+def _gemv(tern, x=A16, xdt=1, M=1, K=128, codes=A16, scales=A16, N=16, y=A16, ydt=0):
+    return tern.lib().tern_gemv(x, xdt, M, K, codes, scales, N, y, ydt, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=17), 1), (dict(M=-1), 1), (dict(N=-3), 1), (dict(K=100), 1), (dict(K=-128), 1),
+    (dict(xdt=2), 4), (dict(ydt=7), 4), (dict(x=NULL), 1), (dict(codes=NULL), 1),
+    (dict(scales=NULL), 1), (dict(y=NULL), 1), (dict(x=A2), 1), (dict(codes=A2), 1),
+])
+def test_gemv_rejects(tern, kw, status):
+    assert _gemv(tern, **kw) == status
+    assert tern.tern_last_error().startswith("tern_gemv")
+
+
+def test_gemv_empty_is_noop(tern):
+    # M == 0 or N == 0 writes nothing and launches nothing
+    assert _gemv(tern, M=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
+    assert _gemv(tern, N=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
+
+
+def _gemm(tern, x=A16, xdt=1, M=64, K=128, codes=A16, scales=A16, N=16, y=A16, ws=NULL, wsb=0):
+    return tern.lib().tern_gemm(x, xdt, M, K, codes, scales, N, y, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=0), 4), (dict(xdt=3), 4), (dict(K=64), 1), (dict(M=-2), 1),
+    (dict(x=NULL), 1), (dict(y=A2), 1), (dict(codes=A2), 1),
+])
+def test_gemm_rejects(tern, kw, status):
+    assert _gemm(tern, **kw) == status
+
+
+def test_gemm_empty_is_noop(tern):
+    assert _gemm(tern, M=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
+
+
+def _fwht(tern, x=A16, xdt=0, signs=NULL, M=1, K=4096, block=4096, inverse=0, y=A16):
+    return tern.lib().tern_fwht(x, xdt, signs, M, K, block, inverse, y, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=3), 1), (dict(block=0), 1), (dict(block=8192, K=8192), 1), (dict(K=6144), 1),
+    (dict(xdt=5), 4), (dict(x=NULL), 1), (dict(y=NULL), 1), (dict(y=A2), 1), (dict(M=-1), 1),
+    (dict(xdt=1), 1),  # bf16 in place (y == x) is rejected
+])
+def test_fwht_rejects(tern, kw, status):
+    assert _fwht(tern, **kw) == status
+
+
+def test_fwht_empty_is_noop(tern):
+    assert _fwht(tern, M=0, x=NULL, y=NULL) == 0
+
+
+def test_codec_rejects(tern):
+    t = np.zeros((2, 128), dtype=np.int8)
+    t[1, 5] = 2
+    s = np.zeros((2, 1), dtype=np.uint16)
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_pack(t, s)
+    assert e.value.status == tern.TERN_ENOTTERNARY
+    t[1, 5] = 1
+    s[0, 0] = 0x7C00  # +inf scale
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_pack(t, s)
+    assert e.value.status == tern.TERN_EINVAL
+    codes = np.full((1, 8), 0x55555555, dtype=np.uint32)
+    codes[0, 7] = 0xD5555555  # slot 15 of word 7 holds 3
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_unpack(codes, 128)
+    assert e.value.status == tern.TERN_EBADCODE
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_dequant_f32(codes, np.zeros((1, 1), np.uint16), 128)
+    assert e.value.status == tern.TERN_EBADCODE
+    lib = tern.lib()
+    assert lib.tern_pack(None, None, 1, 100, None, None) == tern.TERN_EINVAL
+    assert lib.tern_pack(None, None, 0, 128, None, None) == tern.TERN_OK

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Matmul: |y - exact| <= 1e-4 * sum_k |s_g t x_k| per element (bit-exact where
+the arithmetic is exact).  FWHT: relative L2 error <= 1e-5 per row.  Inputs
+are seeded synthetic arrays from synth; expected values come only from the
+oracle.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests._helpers import (assert_fwht_close, assert_matmul_close, big_problem, pack_to_device,
+                            sampled_rows, torch, x_to_device, y_to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tern():
+    T = torch()
+    if not T.cuda.is_available():
+        pytest.skip("no GPU")
+    import ternary_weight_g128_amd as t
+    return t
+
+
+def _x(seed, M, K, xdt):
+    return synth.activations_f32(seed, M, K) if xdt == "f32" else synth.activations_bf16(seed, M, K)
+
+
+def _run_gemv(tern, x, codes_d, scales_d, ydt="f32"):
+    T = torch()
+    out_dtype = T.float32 if ydt == "f32" else T.bfloat16
+    y = tern.tern_gemv(x_to_device(x), codes_d, scales_d, out_dtype=out_dtype)
+    T.cuda.synchronize()
+    return y_to_host(y)
+
+
+# ---------------------------------------------------------------------------
+# GEMV (M <= 16)
+# ---------------------------------------------------------------------------
+
+GEMV_SHAPES = [
+    # (M, K, N): single group, ragged tiles, odd group counts, several tiles
+    (1, 128, 1), (1, 128, 17), (1, 384, 33), (1, 1024, 1024), (2, 640, 100),
+    (3, 1280, 257), (4, 2048, 31), (5, 896, 48), (8, 768, 64), (9, 384, 40),
+    (16, 512, 48), (16, 2304, 300), (1, 4224, 70), (7, 6144, 129),
+]
+
+
+@pytest.mark.parametrize("M,K,N", GEMV_SHAPES)
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_matches_oracle(tern, oracle_lib, M, K, N, xdt):
+    seed = 17 * M + K + 3 * N
+    print(f"gemv M={M} K={K} N={N} x={xdt} seed={seed}", flush=True)
+    t = synth.ternary(seed, N, K)
+    s = synth.scales_f16(seed, N, K)
+    x = _x(seed, M, K, xdt)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y, y_ref, bound, what=f"gemv M{M} K{K} N{N} {xdt}")
+
+
+@pytest.mark.parametrize("M,K,N,xdt", [(1, 1024, 200, "bf16"), (4, 768, 50, "f32"), (16, 256, 20, "bf16")])
+def test_gemv_bf16_output(tern, oracle_lib, M, K, N, xdt):
+    seed = 900 + M
+    t = synth.ternary(seed, N, K)
+    s = synth.scales_f16(seed, N, K)
+    x = _x(seed, M, K, xdt)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d, ydt="bf16")
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y, y_ref, bound, bf16_out=True, what="gemv bf16 out")
+
+
+def test_gemv_zero_weights_exact(tern):
+    K, N = 512, 40
+    t = np.zeros((N, K), dtype=np.int8)
+    s = synth.scales_f16(1, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    for xdt in ("f32", "bf16"):
+        y = _run_gemv(tern, _x(1, 3, K, xdt), codes_d, scales_d)
+        assert (y == 0).all()
+
+
+def test_gemv_identity_exact(tern):
+    K = 1024
+    t = np.eye(K, dtype=np.int8)
+    s = np.full((K, K // 128), 0x3C00, dtype=np.uint16)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    x = synth.activations_bf16(5, 4, K)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    assert np.array_equal(y, (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    xf = synth.activations_f32(5, 2, K)
+    y = _run_gemv(tern, xf, codes_d, scales_d)
+    # binary32 input is carried as two bfloat16 parts: exact to 2^-16 relative
+    assert np.allclose(y, xf.astype(np.float64), rtol=2.0 ** -15, atol=0)
+
+
+def test_gemv_one_hot_exact(tern):
+    K, N = 768, 64
+    s = synth.scales_f16(6, N, K)
+    x = synth.activations_bf16(6, 2, K)
+    rng = np.random.default_rng(6)
+    t = np.zeros((N, K), dtype=np.int8)
+    ks = rng.integers(0, K, size=N)
+    sg = rng.choice([-1, 1], size=N)
+    t[np.arange(N), ks] = sg
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    xv = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sv = s.view(np.float16).astype(np.float64)
+    expect = sg[None, :] * sv[np.arange(N), ks // 128][None, :] * xv[:, ks]
+    # s * x is exact in binary32 (11 x 8 significand bits)
+    assert np.array_equal(y, expect)
+
+
+@pytest.mark.parametrize("M,xdt", [(1, "bf16"), (3, "f32"), (16, "bf16")])
+def test_gemv_integer_inputs_bit_exact(tern, oracle_lib, M, xdt):
+    # integer x in [-64, 64], scales in {0.5, 1, 2}: every partial sum is a
+    # multiple of 0.5 below 2^22, so any summation order is exact
+    K, N = 4096, 96
+    rng = np.random.default_rng(M)
+    t = synth.ternary(40 + M, N, K)
+    s = rng.choice(np.array([0.5, 1.0, 2.0], dtype=np.float16), size=(N, K // 128)).view(np.uint16)
+    xi = rng.integers(-64, 65, size=(M, K)).astype(np.float32)
+    x = xi if xdt == "f32" else ((xi.view(np.uint32) >> 16).astype(np.uint16))
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, _ = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert np.array_equal(y, y_ref)
+
+
+def test_gemv_deterministic(tern):
+    T = torch()
+    K, N = 17408, 640
+    t = synth.ternary(8, N, K)
+    s = synth.scales_f16(8, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    for M, xdt in [(1, "bf16"), (2, "f32"), (16, "bf16")]:
+        xd = x_to_device(_x(8, M, K, xdt))
+        y1 = tern.tern_gemv(xd, codes_d, scales_d)
+        y2 = tern.tern_gemv(xd, codes_d, scales_d)
+        T.cuda.synchronize()
+        assert T.equal(y1, y2)
+
+
+def test_gemv_k_zero_gives_zeros(tern):
+    T = torch()
+    x = T.empty((2, 0), dtype=T.bfloat16, device="cuda")
+    codes = T.empty((5, 0), dtype=T.int32, device="cuda")
+    scales = T.empty((5, 0), dtype=T.int16, device="cuda")
+    y = T.full((2, 5), 7.0, device="cuda")
+    tern.tern_gemv(x, codes, scales, out=y)
+    T.cuda.synchronize()
+    assert (y.cpu() == 0).all()
+
+
+# Full sizes of the decode workloads, in the launch configuration the
+# benchmark uses, checked on sampled output rows (all M for each row).
+FULL = [(1, 1024, 1024, "f32", 1 / 3), (1, 4096, 12288, "f32", 0.35)] + \
+       [(m, k, n, "bf16", 1 / 3) for m in (1, 2, 4, 8, 16) for (k, n) in ((5120, 17408), (17408, 5120))] + \
+       [(1, 5120, 12288, "bf16", 1 / 3), (1, 6144, 5120, "bf16", 1 / 3)]
+
+
+@pytest.mark.parametrize("M,K,N,xdt,p0", FULL)
+def test_gemv_full_size_sampled(tern, oracle_lib, M, K, N, xdt, p0):
+    seed = 1000 + K + N + M
+    print(f"full gemv M={M} K={K} N={N} seed={seed}", flush=True)
+    rows = sampled_rows(N, 160, seed)
+    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, N, K, p0, rows)
+    x = _x(seed, M, K, xdt)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t_rows), s_rows, K)
+    assert_matmul_close(y[:, rows], y_ref, bound, what=f"full M{M} K{K} N{N}")
+
+
+def test_gemv_lm_head_size_sampled(tern, oracle_lib):
+    # the largest single projection of the decode step: 5120 -> 248320
+    K, N, seed = 5120, 248320, 77
+    print("lm-head gemv", flush=True)
+    rows = sampled_rows(N, 96, seed)
+    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, N, K, 1 / 3, rows)
+    x = synth.activations_bf16(seed, 1, K)
+    y = _run_gemv(tern, x, codes_d, scales_d, ydt="bf16")
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t_rows), s_rows, K)
+    assert_matmul_close(y[:, rows], y_ref, bound, bf16_out=True, what="lm head")
+
+
+# ---------------------------------------------------------------------------
+# FWHT
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,block", [(1, 4096, 4096), (3, 8192, 4096), (2, 4096, 1024), (1, 512, 64),
+                                       (5, 96, 32), (2, 64, 2), (1, 16, 1), (2, 3 * 256, 256)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("signed", [True, False])
+def test_fwht_matches_oracle(tern, oracle_lib, M, K, block, xdt, signed):
+    seed = M * 31 + K + block
+    x = _x(seed, M, K, xdt)
+    d = synth.signs(seed, K) if signed else None
+    xd = x_to_device(x)
+    dd = torch().from_numpy(d).cuda() if signed else None
+    x64 = x.astype(np.float64) if xdt == "f32" else oracle_lib.bf16_bits_to_f64(x)
+    y = tern.tern_fwht(xd, dd, block)
+    yi = tern.tern_fwht(y, dd, block, inverse=True)
+    torch().cuda.synchronize()
+    assert_fwht_close(y_to_host(y), oracle_lib.fwht(x64, d, block), what="forward")
+    assert_fwht_close(y_to_host(yi), oracle_lib.fwht(y_to_host(y), d, block, inverse=True), what="inverse")
+    # forward then inverse returns x
+    assert_fwht_close(y_to_host(yi), x64, what="round trip")
+
+
+def test_fwht_in_place(tern, oracle_lib):
+    T = torch()
+    x = synth.activations_f32(3, 2, 8192)
+    d = synth.signs(3, 8192)
+    xd = x_to_device(x)
+    tern.tern_fwht(xd, T.from_numpy(d).cuda(), 4096, out=xd)
+    T.cuda.synchronize()
+    assert_fwht_close(y_to_host(xd), oracle_lib.fwht(x.astype(np.float64), d, 4096), what="in place")
+
+
+def test_fwht_closed_forms(tern):
+    T = torch()
+    e0 = T.zeros((1, 4096), device="cuda")
+    e0[0, 0] = 1.0
+    y = tern.tern_fwht(e0, None, 4096)
+    T.cuda.synchronize()
+    assert (y.cpu() == 1.0 / 64).all()     # normalization 2^-6 is exact
+    ones = T.ones((1, 4096), device="cuda")
+    y = tern.tern_fwht(ones, None, 4096).cpu()
+    assert y[0, 0] == 64.0 and (y[0, 1:] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Rotated decode: sign flip + FWHT (block 4096) + GEMV at the full size
+# ---------------------------------------------------------------------------
+
+def test_rotated_decode_full_size(tern, oracle_lib):
+    w = synth.ROTATED
+    seed = 2024
+    print("rotated decode", flush=True)
+    rows = sampled_rows(w.N, 200, seed)
+    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, w.N, w.K, w.p_zero, rows)
+    x = synth.activations_bf16(seed, w.M, w.K)
+    d = synth.signs(seed, w.K)
+    T = torch()
+    xr = tern.tern_fwht(x_to_device(x), T.from_numpy(d).cuda(), w.rotate_block)
+    y = tern.tern_gemv(xr, codes_d, scales_d)
+    T.cuda.synchronize()
+    xr_h = y_to_host(xr)
+    xr_ref = oracle_lib.fwht(oracle_lib.bf16_bits_to_f64(x), d, w.rotate_block)
+    assert_fwht_close(xr_h, xr_ref, what="rotation")
+    # the GEMV on the rotation it was given ...
+    codes_o = oracle_lib.encode(t_rows)
+    y_ref, bound = oracle_lib.matmul(xr_h.astype(np.float32), codes_o, s_rows, w.K)
+    assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound, what="gemv on rotated x")
+    # ... and end to end against the FP64 rotation (its own error adds
+    # sum |s t| * |dx| <= sum |s t| * 1e-5 * ||x'|| per output)
+    y64, b64 = oracle_lib.matmul(xr_ref, codes_o, s_rows, w.K)
+    dx = np.abs(xr_h - xr_ref)
+    wabs = np.abs(oracle_lib.dequant(codes_o, s_rows, w.K))
+    # allowance 1e-4 * B + sum |s t| |dx|, expressed through the bound
+    assert_matmul_close(y_to_host(y)[:, rows], y64, b64 + 1e4 * (dx @ wabs.T),
+                        what="rotated decode end to end")
+
+
+# ---------------------------------------------------------------------------
+# GEMM (any M)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 64), (17, 640, 100), (64, 1024, 128), (100, 384, 257),
+                                   (130, 2048, 96), (256, 1280, 320)])
+def test_gemm_matches_oracle(tern, oracle_lib, M, K, N):
+    seed = 5 * M + K + N
+    print(f"gemm M={M} K={K} N={N}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = tern.tern_gemm(x_to_device(x), codes_d, scales_d)
+    torch().cuda.synchronize()
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y_to_host(y), y_ref, bound, what=f"gemm M{M} K{K} N{N}")
+
+
+@pytest.mark.parametrize("K,N", [(5120, 17408), (17408, 5120)])
+def test_gemm_prefill_full_size_sampled(tern, oracle_lib, K, N):
+    M, seed = 512, 4000 + K
+    print(f"prefill gemm K={K} N={N}", flush=True)
+    rows = sampled_rows(N, 48, seed)
+    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, N, K, 0.35, rows)
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    y = tern.tern_gemm(x_to_device(x), codes_d, scales_d)
+    torch().cuda.synchronize()
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t_rows), s_rows, K)
+    assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound, what=f"prefill K{K} N{N}")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture of the decode step: every replay equals eager execution
+# ---------------------------------------------------------------------------
+
+def test_rotated_step_graph_replays_match_eager(tern):
+    T = torch()
+    K, N, seed = 4096, 1000, 31
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    xd = x_to_device(synth.activations_bf16(seed, 1, K))
+    dd = T.from_numpy(synth.signs(seed, K)).cuda()
+    xr = T.empty((1, K), dtype=T.float32, device="cuda")
+    y = T.empty((1, N), dtype=T.float32, device="cuda")
+
+    def step():
+        tern.tern_fwht(xd, dd, 4096, out=xr)
+        tern.tern_gemv(xr, codes_d, scales_d, out=y)
+
+    step()
+    T.cuda.synchronize()
+    y_eager = y.clone()
+    g = T.cuda.CUDAGraph()
+    st = T.cuda.Stream()
+    st.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(st):
+        with T.cuda.graph(g, stream=st):
+            step()
+    T.cuda.current_stream().wait_stream(st)
+    for r in range(4):
+        y.zero_()
+        xr.zero_()
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, y_eager), f"replay {r}"
+        step()                      # eager work between replays
+        T.cuda.synchronize()
