@@ -126,7 +126,7 @@ tern_status tern_dequant_f32(const uint32_t *codes, const uint16_t *s_f16,
  * section 3), in natural Sylvester order H[i][l] = (-1)^popcount(i & l):
  *   inverse == 0:  y[m, jb+i] = b^-1/2 sum_l H[i][l] d[jb+l] x[m, jb+l]
  *   inverse != 0:  y[m, jb+i] = d[jb+i] b^-1/2 sum_l H[i][l] x[m, jb+l]
- * x: [M][K] TERN_F32 or TERN_BF16; signs: int8 [K] of +-1, or NULL for all +1
+ * x: [M][K] TERN_F32 or TERN_BF16; signs: int8 [K] of +-1 (16-byte aligned), or NULL for all +1
  * (other values are multiplied in as given); y: float [M][K], which may be
  * the same buffer as x when xdt == TERN_F32.  block: a power of two in
  * [1, 4096]; K % block == 0.  x and y 16-byte aligned.

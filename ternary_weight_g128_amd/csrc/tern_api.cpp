@@ -142,8 +142,8 @@ tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, in
         set_error("tern_fwht: NULL pointer");
         return TERN_EINVAL;
     }
-    if (!aligned(x, 16) || !aligned(y, 16)) {
-        set_error("tern_fwht: x and y must be 16-byte aligned");
+    if (!aligned(x, 16) || !aligned(y, 16) || (signs && !aligned(signs, 16))) {
+        set_error("tern_fwht: x, y and signs must be 16-byte aligned");
         return TERN_EINVAL;
     }
     if (xdt == TERN_BF16 && static_cast<const void *>(y) == x) {

@@ -81,172 +81,270 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b)
 // ---------------------------------------------------------------------------
 //
 // Work decomposition.  A workgroup owns TPW consecutive 16-row tiles and the
-// whole K; its W waves split K into contiguous ranges of whole 128-K groups
-// and the partial sums are combined in LDS in a fixed order at the end (so
-// the result is deterministic).  Within a wave, lane l serves output row
-// n0 + 16*tile + (l & 15) and lane group g = l >> 4 (the MFMA k-slot group).
+// whole K; its W waves split K into contiguous ranges of whole 256-K blocks
+// (two scale groups) and the partial sums are combined in LDS in a fixed
+// order at the end, so the result is deterministic.  Within a wave, lane l
+// serves output row n0 + 16*tile + (l & 15) and lane group g = l >> 4 (the
+// MFMA k-slot group).
 //
-// Codes.  Per 256-K block (two groups) each lane loads one 16-byte vector:
-// words 4g..4g+3 of its row's 64-byte block segment, so the four lanes of a
-// row read 64 contiguous bytes.  A v_permlane32_swap pair then regroups the
-// words so that every lane holds two words of group 0 and two of group 1
-// (the MFMA contracts over all four lane groups, which must therefore see
-// the same scale group).  After the swap, word w of a group sits in lane
-// group G(w) = {0, 2, 1, 3}[w >> 1] as operand half w & 1.
+// Codes.  Per block each lane loads one 16-byte vector per tile: words
+// 4g..4g+3 of its row's 64-byte block segment, so the four lanes of a row
+// read 64 contiguous bytes.  A v_permlane32_swap pair then regroups the words
+// so that every lane holds two words of group 0 and two of group 1 (the MFMA
+// contracts over all four lane groups, which must therefore see the same
+// scale group).  After the swap, word w of a group sits in lane group
+// {0, 2, 1, 3}[w >> 1] as operand half w & 1.
 //
 // Activations.  The MFMA A operand is x: row i = l & 15 of A is activation
 // row i (bfloat16 input) or, for binary32 input, rows 2m / 2m + 1 hold the
-// bfloat16 high part and the bfloat16 remainder of x[m] (x - hi is exact in
-// binary32 and the two parts together carry 16 significand bits).  Each
-// wave stages the activations of its K range in LDS, permuted so that one
-// 16-byte LDS read gives a lane its A operand for one MFMA; rows that do not
-// exist read nothing and stay zero.
-//
-// LDS layout of the staged activations, in bfloat16 elements, for local
-// group gl, MFMA index mu = 2 * (operand half) + h, lane group g, A row r and
-// element e:  ((((gl * 4 + mu) * 4 + g) * MX + r) * 8 + e).
+// bfloat16 rounding of x[m] and the bfloat16 rounding of the remainder
+// (x - hi is exact in binary32; the two parts carry 16 significand bits).
+// The workgroup stages x for all of K in LDS once, permuted so that one
+// 16-byte LDS read gives a lane its A operand for one MFMA; lanes whose A row
+// does not exist never read and keep zeros.  LDS layout in bfloat16
+// elements, for scale group G, MFMA index mu = 2 * (operand half) + h, lane
+// group g, A row r and element e: ((((G * 4 + mu) * 4 + g) * MX + r) * 8 + e),
+// where element e of (G, mu, g) holds k = 128 G + 16 w + 4 h + (e >> 1) +
+// 8 (e & 1) for the word w = 2 {0, 2, 1, 3}[g] + (mu >> 1).
 
-template <int MX, bool XF32>
-__device__ __forceinline__ void stage_activations(
-    __bf16 *__restrict__ lds, const void *__restrict__ x, int M, int64_t K,
-    int g_begin, int ngroups, int lane)
+struct GemvArgs {
+    const void *x;
+    const uint32_t *codes;
+    const uint16_t *scales;
+    void *y;
+    int64_t N;
+    int K;        // multiple of 128
+    int M;        // rows of x
+    int nblk;     // 256-K blocks in K (the last one may hold one group)
+    int wk;       // waves of a workgroup that split K (they share tiles)
+    int wt;       // waves of a workgroup that split tiles (wt * wk waves)
+    int bq, br;   // blocks per K-wave: bq, plus one for the first br K-waves
+    int y_bf16;
+};
+
+// One staging unit: the 16 activations of word wi (k = 16 wi .. 16 wi + 15)
+// of row m, held as 32-bit words: bf16 pairs, or binary32 values.
+template <bool XF32>
+struct XUnit {
+    uint32_t v[XF32 ? 16 : 8];
+};
+
+template <bool XF32>
+__device__ __forceinline__ void load_unit(XUnit<XF32> &u, const GemvArgs &a, int m, int wi)
 {
-    const int nwords = ngroups * kWordsPerGroup;
-    const int mrows = M;  // source rows
-    for (int u = lane; u < mrows * nwords; u += 64) {
-        const int m = u / nwords;
-        const int wi = u - m * nwords;
-        const int gl = wi >> 3, w = wi & 7;
-        const int half_sel = w & 1;
-        const int g = ((w >> 1) == 1) ? 2 : (((w >> 1) == 2) ? 1 : (w >> 1));
-        const int64_t k0 = (int64_t)g_begin * kGroup + (int64_t)wi * 16;
-        float v[16];
-        if constexpr (XF32) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                static_cast<const float *>(x) + (int64_t)m * K + k0);
+    if constexpr (XF32) {
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+            static_cast<const float *>(a.x) + (int64_t)m * a.K + 16 * wi);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float4 f = src[q];
-                v[4 * q + 0] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-            }
-        } else {
-            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
-                static_cast<const uint16_t *>(x) + (int64_t)m * K + k0);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                u32x4_t d = src[q];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[8 * q + 2 * e + 0] = bf16_to_float((uint16_t)(d[e] & 0xffffu));
-                    v[8 * q + 2 * e + 1] = bf16_to_float((uint16_t)(d[e] >> 16));
-                }
-            }
+        for (int q = 0; q < 4; ++q) {
+            u32x4_t d = src[q];
+            u.v[4 * q + 0] = d[0]; u.v[4 * q + 1] = d[1]; u.v[4 * q + 2] = d[2]; u.v[4 * q + 3] = d[3];
         }
+    } else {
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.x) + (int64_t)m * a.K + 16 * wi);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int mu = 2 * half_sel + h;
-            u16x8_t hi, lo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = v[4 * h + (e >> 1) + 8 * (e & 1)];
-                if constexpr (XF32) {
-                    const uint16_t hb = float_to_bf16_rne(f);
-                    hi[e] = hb;
-                    lo[e] = float_to_bf16_rne(f - bf16_to_float(hb));
-                } else {
-                    hi[e] = (uint16_t)(__builtin_bit_cast(uint32_t, f) >> 16);
-                }
-            }
-            const int base = ((gl * 4 + mu) * 4 + g) * MX;
-            if constexpr (XF32) {
-                *reinterpret_cast<u16x8_t *>(lds + (base + 2 * m) * 8) = hi;
-                *reinterpret_cast<u16x8_t *>(lds + (base + 2 * m + 1) * 8) = lo;
-            } else {
-                *reinterpret_cast<u16x8_t *>(lds + (base + m) * 8) = hi;
-            }
+        for (int q = 0; q < 2; ++q) {
+            u32x4_t d = src[q];
+            u.v[4 * q + 0] = d[0]; u.v[4 * q + 1] = d[1]; u.v[4 * q + 2] = d[2]; u.v[4 * q + 3] = d[3];
         }
     }
 }
 
-template <int MX, bool XF32, int TPW, int PF>
-__global__ __launch_bounds__(512) void gemv_kernel(
-    const void *__restrict__ x, int M, int64_t K, const uint32_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, int64_t N, void *__restrict__ y, int y_bf16,
-    int waves, int wave_groups)
+// Write one unit into the permuted LDS image: two 16-byte chunks per A row.
+template <int MX, bool XF32>
+__device__ __forceinline__ void store_unit(__bf16 *lds, const XUnit<XF32> &u, int m, int wi)
 {
+    const int G = wi >> 3, w = wi & 7;
+    const int g = ((w >> 1) == 1) ? 2 : (((w >> 1) == 2) ? 1 : (w >> 1));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int mu = 2 * (w & 1) + h;
+        const int base = ((G * 4 + mu) * 4 + g) * MX;
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            // element pair (2v, 2v + 1) holds k = 4h + v and 4h + v + 8
+            const int ka = 4 * h + v, kb = ka + 8;
+            if constexpr (XF32) {
+                const float fa = __builtin_bit_cast(float, u.v[ka]);
+                const float fb = __builtin_bit_cast(float, u.v[kb]);
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                const bf16x2_t ph = {(__bf16)fa, (__bf16)fb};
+                const bf16x2_t pl = {(__bf16)(fa - (float)ph[0]), (__bf16)(fb - (float)ph[1])};
+                hi[v] = __builtin_bit_cast(uint32_t, ph);
+                lo[v] = __builtin_bit_cast(uint32_t, pl);
+            } else {
+                // bf16 pairs arrive as (k even, k odd) halves of 32-bit words
+                const uint32_t wa = u.v[ka >> 1], wb = u.v[kb >> 1];
+                const uint32_t sa = (ka & 1) ? (wa >> 16) : (wa & 0xffffu);
+                const uint32_t sb = (kb & 1) ? (wb & 0xffff0000u) : (wb << 16);
+                hi[v] = sa | sb;
+            }
+        }
+        if constexpr (XF32) {
+            *reinterpret_cast<u32x4_t *>(lds + (base + 2 * m) * 8) = hi;
+            *reinterpret_cast<u32x4_t *>(lds + (base + 2 * m + 1) * 8) = lo;
+        } else {
+            *reinterpret_cast<u32x4_t *>(lds + (base + m) * 8) = hi;
+        }
+    }
+}
+
+// Scale of block j of a quad for lane group 0, when lane group g holds the
+// scale pair of block g of the quad: v_permlane16_swap moves rows 1 -> 0 and
+// 3 -> 2, v_permlane32_swap moves rows 2, 3 -> 0, 1.
+__device__ __forceinline__ uint32_t quad_scale(uint32_t sq, int j)
+{
+    if (j == 0) return sq;
+    if (j == 1) return __builtin_amdgcn_permlane16_swap(sq, sq, false, false)[1];
+    const uint32_t r2 = __builtin_amdgcn_permlane32_swap(sq, sq, false, false)[1];
+    if (j == 2) return r2;
+    return __builtin_amdgcn_permlane16_swap(r2, r2, false, false)[1];
+}
+
+// PF == 4: the code ring holds one quad of four 256-K blocks.  For MX <= 4
+// every live output row sits in lane group 0, so the scales of a quad come
+// from one load per lane (lane group g loads block g's scale pair) and are
+// redistributed with cross-row swaps; for larger MX each lane loads its
+// row's pair per block.
+template <int MX, bool XF32, int TPW, bool SC4>
+__global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
+{
+    constexpr int PF = 4;
+    constexpr bool kQuadScales = MX <= 4;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int kRowsOut = (MX < 4) ? MX : 4;  // accumulator rows per lane that can be live
+    constexpr int kUB = XF32 ? 2 : 4;            // staging units per thread per batch
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = blockDim.x >> 6;
+    const int kw = wave % a.wk;                  // which K range
+    const int tw = wave / a.wk;                  // which tiles
     const int nn = lane & 15;
     const int g = lane >> 4;
     const int arow = lane & 15;
-    const int Mx = XF32 ? 2 * M : M;
+    const int Mx = XF32 ? 2 * a.M : a.M;
     const bool a_active = arow < Mx;
+    const int G = a.K / kGroup;
 
-    const int G = (int)(K / kGroup);
-    const int g_begin = (int)(((int64_t)wave * G) / waves);
-    const int g_end = (int)(((int64_t)(wave + 1) * G) / waves);
-    const int ngroups = g_end - g_begin;
-    const int nblocks = (ngroups + 1) >> 1;
+    const int b_begin = kw * a.bq + (kw < a.br ? kw : a.br);
+    const int nblocks = a.bq + (kw < a.br ? 1 : 0);
+    const int g_begin = 2 * b_begin;
+    const int g_end = (g_begin + 2 * nblocks < G) ? g_begin + 2 * nblocks : G;
 
-    const int64_t n0 = (int64_t)blockIdx.x * (kTileN * TPW);
-    const int64_t words_per_row = K / 16;
-    const int64_t groups_per_row = K / kGroup;
+    const int rows_per_wg = kTileN * TPW * a.wt;
+    const int64_t n_wg = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t n0 = n_wg + (int64_t)tw * (kTileN * TPW);
+    if (a.K == 0) {  // empty sum: zeros (uniform branch before any load)
+        for (int o = threadIdx.x; o < a.M * rows_per_wg; o += blockDim.x) {
+            const int64_t n = n_wg + o % rows_per_wg;
+            if (n < a.N) {
+                const int m = o / rows_per_wg;
+                if (a.y_bf16)
+                    static_cast<uint16_t *>(a.y)[(int64_t)m * a.N + n] = 0;
+                else
+                    static_cast<float *>(a.y)[(int64_t)m * a.N + n] = 0.0f;
+            }
+        }
+        return;
+    }
+    // From here on K > 0, so every wave has at least one block and every
+    // thread a staging unit; the loads below are unconditional so that the
+    // compiler can count outstanding loads exactly.
+    __bf16 *lds_x = reinterpret_cast<__bf16 *>(smem);
+    float *red = reinterpret_cast<float *>(smem + (size_t)a.K * MX * 2);
 
-    // wave-private activation staging area (wave_groups = largest wave range)
-    __bf16 *lds_x = reinterpret_cast<__bf16 *>(smem) +
-                    (size_t)wave * wave_groups * kGroup * MX;
-    float *red = reinterpret_cast<float *>(smem + (size_t)waves * wave_groups * kGroup * MX * 2);
+    // 1. activation loads for the first staging batch go out first, so that
+    //    waiting for them does not wait for the code stream issued next.
+    //    Unit indices past the end are clamped to the last unit: duplicate
+    //    stores write the same values to the same LDS bytes.
+    const int wpr = a.K / 16;  // words (units) per activation row
+    const int units = a.M * wpr;
+    const int nthreads = 64 * waves;
+    XUnit<XF32> xu[kUB];
+#pragma unroll
+    for (int i = 0; i < kUB; ++i) {
+        int u = threadIdx.x + i * nthreads;
+        u = u < units ? u : units - 1;
+        load_unit<XF32>(xu[i], a, u / wpr, u % wpr);
+    }
 
+    // 2. code stream: one quad ahead
     const uint32_t *crow[TPW];
     const uint16_t *srow[TPW];
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
         int64_t r = n0 + tp * kTileN + nn;
-        if (r > N - 1) r = N - 1;  // rows past N load a valid row; results are dropped
-        crow[tp] = codes + r * words_per_row;
-        srow[tp] = scales + r * groups_per_row;
+        if (r > a.N - 1) r = a.N - 1;  // rows past N load a valid row; results are dropped
+        crow[tp] = a.codes + r * (a.K / 16);
+        srow[tp] = a.scales + r * G;
     }
-
-    float yacc[TPW][kRowsOut];
-#pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
-#pragma unroll
-        for (int v = 0; v < kRowsOut; ++v) yacc[tp][v] = 0.0f;
-
     u32x4_t cbuf[PF][TPW];
-    uint32_t sbuf[PF][TPW][2];
-
-    // Block b covers local groups 2b and 2b + 1 (the second may not exist
-    // at the end of an odd range).  Loads stay branch-free and in bounds: for
-    // a one-group block the upper lane groups re-read the first group, whose
-    // second-half contribution is multiplied by a zero scale.  Loaded values
-    // are not touched until they are consumed PF blocks later.
-    auto load_block = [&](int b, u32x4_t (&c)[TPW], uint32_t (&s)[TPW][2]) {
+    uint32_t sbuf[PF][TPW];    // per-block scale pairs (MX > 4)
+    uint32_t squad[TPW];       // quad scale pairs (MX <= 4)
+    // For a one-group block the upper lane groups re-read the first group,
+    // whose second-half contribution is multiplied by a zero scale.
+    auto scale_pair = [&](int tp, int gb, bool two) -> uint32_t {
+        if constexpr (SC4)
+            return *reinterpret_cast<const uint32_t *>(srow[tp] + gb);
+        else
+            return (uint32_t)srow[tp][gb] | ((uint32_t)srow[tp][two ? gb + 1 : gb] << 16);
+    };
+    auto load_block = [&](int b, int p) {
+        b = b < nblocks ? b : nblocks - 1;
         const int gb = g_begin + 2 * b;
         const bool two = (gb + 1) < g_end;
         const int lg = two ? g : (g & 1);
 #pragma unroll
         for (int tp = 0; tp < TPW; ++tp) {
-            c[tp] = *reinterpret_cast<const u32x4_t *>(crow[tp] + (int64_t)gb * kWordsPerGroup + 4 * lg);
-            s[tp][0] = srow[tp][gb];
-            s[tp][1] = srow[tp][two ? gb + 1 : gb];
+            cbuf[p][tp] = *reinterpret_cast<const u32x4_t *>(crow[tp] + gb * kWordsPerGroup + 4 * lg);
+            if constexpr (!kQuadScales) sbuf[p][tp] = scale_pair(tp, gb, two);
         }
     };
-
-    // Start the code stream, then stage this wave's activations once; the
-    // loop below issues no branch that touches memory, so loads stay in
-    // flight across blocks.
-    if (nblocks > 0) {
+    auto load_quad_scales = [&](int b0) {
+        if constexpr (kQuadScales) {
+            int b = b0 + g;
+            b = b < nblocks ? b : nblocks - 1;
+            const int gb = g_begin + 2 * b;
+            const bool two = (gb + 1) < g_end;
 #pragma unroll
-        for (int p = 0; p < PF; ++p) load_block(p < nblocks ? p : nblocks - 1, cbuf[p], sbuf[p]);
+            for (int tp = 0; tp < TPW; ++tp) squad[tp] = scale_pair(tp, gb, two);
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_block(p, p);
+    load_quad_scales(0);
+
+    // 3. stage the activations of all of K (shared by the waves)
+#pragma unroll
+    for (int i = 0; i < kUB; ++i) {
+        int u = threadIdx.x + i * nthreads;
+        u = u < units ? u : units - 1;
+        store_unit<MX, XF32>(lds_x, xu[i], u / wpr, u % wpr);
     }
-    stage_activations<MX, XF32>(lds_x, x, M, K, g_begin, ngroups, lane);
+    for (int u0 = kUB * nthreads; u0 < units; u0 += kUB * nthreads) {
+#pragma unroll
+        for (int i = 0; i < kUB; ++i) {
+            int u = u0 + threadIdx.x + i * nthreads;
+            u = u < units ? u : units - 1;
+            load_unit<XF32>(xu[i], a, u / wpr, u % wpr);
+        }
+#pragma unroll
+        for (int i = 0; i < kUB; ++i) {
+            int u = u0 + threadIdx.x + i * nthreads;
+            u = u < units ? u : units - 1;
+            store_unit<MX, XF32>(lds_x, xu[i], u / wpr, u % wpr);
+        }
+    }
     __syncthreads();
 
-    // A operands persist across blocks: lanes whose A row does not exist
-    // never load and keep zeros; the rows they feed are discarded anyway.
+    // 4. stream the codes
+    float yacc[TPW][kRowsOut];
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int v = 0; v < kRowsOut; ++v) yacc[tp][v] = 0.0f;
     bf16x8_t a0[4], a1[4];
 #pragma unroll
     for (int mu = 0; mu < 4; ++mu) {
@@ -258,12 +356,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(
     constexpr int kMuStride = 4 * MX * 8;
 
     // One block: A operands from LDS, consume ring slot p (regroup and flip
-    // the code words into fresh registers), optionally refill the slot, then
-    // two interleaved 4-MFMA chains (one per 128-K group) and the per-group
-    // scaling in binary32.
-    auto process = [&](int b, int p, bool refill) {
-        const int gl0 = 2 * b;
-        const bool two = gl0 + 1 < ngroups;
+    // the code words into fresh registers), refill the slot, then two
+    // interleaved 4-MFMA chains per tile (one per 128-K group) and the
+    // per-group scaling in binary32.
+    auto process = [&](int b, int p, const uint32_t (&sq)[TPW], bool refill) {
+        const int gl0 = g_begin + 2 * b;
+        const bool two = gl0 + 1 < g_end;
         if (a_active) {
             const __bf16 *pa0 = lds_lane + gl0 * kGroupStride;
             const __bf16 *pa1 = pa0 + (two ? kGroupStride : 0);
@@ -283,44 +381,71 @@ __global__ __launch_bounds__(512) void gemv_kernel(
             wq[tp][1] = s13[0] ^ kFlip;  // group 0, operand half 1
             wq[tp][2] = s02[1] ^ kFlip;  // group 1, operand half 0
             wq[tp][3] = s13[1] ^ kFlip;  // group 1, operand half 1
-            sc[tp][0] = half_to_float((uint16_t)sbuf[p][tp][0]);
-            sc[tp][1] = two ? half_to_float((uint16_t)sbuf[p][tp][1]) : 0.0f;
+            const uint32_t pair = kQuadScales ? quad_scale(sq[tp], p) : sbuf[p][tp];
+            sc[tp][0] = half_to_float((uint16_t)(pair & 0xffffu));
+            sc[tp][1] = two ? half_to_float((uint16_t)(pair >> 16)) : 0.0f;
         }
-        if (refill) {
-            const int nb = (b + PF < nblocks) ? b + PF : nblocks - 1;
-            load_block(nb, cbuf[p], sbuf[p]);
-        }
+        if (refill) load_block(b + PF, p);
+        f32x4_t acc0[TPW], acc1[TPW];
 #pragma unroll
         for (int tp = 0; tp < TPW; ++tp) {
-            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[0], weights_operand(wq[tp][0], 0), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], weights_operand(wq[tp][2], 0), acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[1], weights_operand(wq[tp][0], 1), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[1], weights_operand(wq[tp][2], 1), acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[2], weights_operand(wq[tp][1], 0), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[2], weights_operand(wq[tp][3], 0), acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[3], weights_operand(wq[tp][1], 1), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[3], weights_operand(wq[tp][3], 1), acc1, 0, 0, 0);
+            acc0[tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc1[tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-            for (int v = 0; v < kRowsOut; ++v) {
-                yacc[tp][v] = __builtin_fmaf(sc[tp][0], acc0[v], yacc[tp][v]);
-                yacc[tp][v] = __builtin_fmaf(sc[tp][1], acc1[v], yacc[tp][v]);
+        for (int mu = 0; mu < 4; ++mu) {
+#pragma unroll
+            for (int tp = 0; tp < TPW; ++tp) {
+                acc0[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a0[mu], weights_operand(wq[tp][mu >> 1], mu & 1), acc0[tp], 0, 0, 0);
+                acc1[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a1[mu], weights_operand(wq[tp][2 + (mu >> 1)], mu & 1), acc1[tp], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+            for (int v = 0; v < kRowsOut; ++v) {
+                yacc[tp][v] = __builtin_fmaf(sc[tp][0], acc0[tp][v], yacc[tp][v]);
+                yacc[tp][v] = __builtin_fmaf(sc[tp][1], acc1[tp][v], yacc[tp][v]);
+            }
     };
 
-    if (nblocks > 0) {
-        const int nfull = (nblocks / PF) * PF;
-        for (int b0 = 0; b0 < nfull; b0 += PF) {
+    const int nfull = (nblocks / PF) * PF;
+    for (int b0 = 0; b0 < nfull; b0 += PF) {
+        uint32_t sq[TPW];
 #pragma unroll
-            for (int p = 0; p < PF; ++p) process(b0 + p, p, true);
-        }
+        for (int tp = 0; tp < TPW; ++tp) sq[tp] = squad[tp];
+        load_quad_scales(b0 + PF);
 #pragma unroll
-        for (int p = 0; p < PF; ++p)
-            if (nfull + p < nblocks) process(nfull + p, p, false);
+        for (int p = 0; p < PF; ++p) process(b0 + p, p, sq, true);
     }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (nfull + p < nblocks) process(nfull + p, p, squad, false);
 
-    // Cross-wave reduction in a fixed order.  red[wave][tile][A row][16]
+    // 5. combine the K-waves' partial sums in a fixed order and store
+    auto store = [&](int m, int64_t n, float sum) {
+        const float out = -0.5f * sum;  // operands carried -2t
+        if (a.y_bf16)
+            static_cast<uint16_t *>(a.y)[(int64_t)m * a.N + n] = float_to_bf16_rne(out);
+        else
+            static_cast<float *>(a.y)[(int64_t)m * a.N + n] = out;
+    };
+    if (a.wk == 1) {
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            const int64_t n = n0 + tp * kTileN + nn;
+#pragma unroll
+            for (int v = 0; v < kRowsOut; v += (XF32 ? 2 : 1)) {
+                const int i = 4 * g + v;
+                const int m = XF32 ? i / 2 : i;
+                if (m < a.M && n < a.N)
+                    store(m, n, XF32 ? yacc[tp][v] + yacc[tp][v + 1] : yacc[tp][v]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
@@ -329,149 +454,276 @@ __global__ __launch_bounds__(512) void gemv_kernel(
             if (i < MX) red[((wave * TPW + tp) * MX + i) * kTileN + nn] = yacc[tp][v];
         }
     __syncthreads();
-    const int outs = M * kTileN * TPW;
+    const int outs = a.M * rows_per_wg;
     for (int o = threadIdx.x; o < outs; o += blockDim.x) {
-        const int m = o / (kTileN * TPW);
-        const int rem = o - m * (kTileN * TPW);
-        const int tp = rem / kTileN, j = rem - tp * kTileN;
-        const int64_t n = n0 + tp * kTileN + j;
-        if (n >= N) continue;
+        const int m = o / rows_per_wg;
+        const int rem = o - m * rows_per_wg;           // row within the workgroup
+        const int twi = rem / (kTileN * TPW);          // tile-wave
+        const int tp = (rem / kTileN) % TPW, j = rem % kTileN;
+        const int64_t n = n_wg + rem;
+        if (n >= a.N) continue;
         float sum = 0.0f;
-        for (int w = 0; w < waves; ++w) {
-            const float *base = red + ((w * TPW + tp) * MX) * kTileN;
+        for (int w = 0; w < a.wk; ++w) {
+            const float *base = red + (((twi * a.wk + w) * TPW + tp) * MX) * kTileN;
             if constexpr (XF32)
                 sum += base[(2 * m) * kTileN + j] + base[(2 * m + 1) * kTileN + j];
             else
                 sum += base[m * kTileN + j];
         }
-        const float out = -0.5f * sum;  // operands carried -2t
-        if (y_bf16)
-            static_cast<uint16_t *>(y)[(int64_t)m * N + n] = float_to_bf16_rne(out);
-        else
-            static_cast<float *>(y)[(int64_t)m * N + n] = out;
+        store(m, n, sum);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Signed normalized Walsh-Hadamard transform: one workgroup per (row, block)
+// Signed normalized Walsh-Hadamard transform
 // ---------------------------------------------------------------------------
+//
+// Natural (Sylvester) order: H[i][l] = (-1)^popcount(i & l), so the
+// transform is a butterfly (a, c) -> (a + c, a - c) over every index bit.
+// For blocks of b = 2^L >= 16 elements a workgroup handles BPW blocks of one
+// row with b/16 threads per block; each thread holds 16 values whose index
+// differs in four "register bits" and applies the butterflies over those bits
+// in registers.  Between passes the values go through LDS so that the next
+// four index bits become register bits.  LDS index i is padded to
+// i + i / 16, which keeps the strided transposes free of bank conflicts.
+// binary32 throughout; the 1/sqrt(b) factor is applied once at the end (a
+// power of two, so exact, when L is even).
+
+// Element index for thread t (within a block) and register index r when the
+// register bits start at bit rb.
+__device__ __forceinline__ int fwht_index(int t, int r, int rb)
+{
+    return (t & ((1 << rb) - 1)) | (r << rb) | ((t >> rb) << (rb + 4));
+}
+
+__device__ __forceinline__ int fwht_pad(int i) { return i + (i >> 4); }
+
+__device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_hi)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < j_lo || j >= j_hi) continue;
+        const int h = 1 << j;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (r & h) continue;
+            const float a = v[r], c = v[r | h];
+            v[r] = a + c;
+            v[r | h] = a - c;
+        }
+    }
+}
+
 template <bool XF32>
-__global__ __launch_bounds__(256) void fwht_kernel(
-    const void *__restrict__ x, const int8_t *__restrict__ signs, int64_t M, int64_t K,
-    int block, int log2b, int inverse, float *y, float norm)
+__global__ __launch_bounds__(256) void fwht16_kernel(
+    const void *__restrict__ x, const int8_t *__restrict__ signs, int64_t M, int64_t K, int L,
+    int bpw, int inverse, float *y, float norm)
 {
     extern __shared__ float buf[];
-    const int64_t sbase = (int64_t)blockIdx.x * block;
+    const int b = 1 << L;
+    const int tpb = b >> 4;                       // threads per block
+    const int jb = threadIdx.x / tpb;             // block within the workgroup
+    const int t = threadIdx.x - jb * tpb;         // thread within the block
+    const int64_t blocks_per_row = K >> L;
+    const int64_t blk = (int64_t)blockIdx.x * bpw + jb;
+    const bool live = jb < bpw && blk < blocks_per_row;
+    const int64_t sbase = (blk < blocks_per_row ? blk : 0) << L;
+    float *lb = buf + (size_t)jb * fwht_pad(b);
     for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
-    const int64_t base = m * K + sbase;
-    for (int i = threadIdx.x; i < block; i += blockDim.x) {
-        float v;
-        if constexpr (XF32)
-            v = static_cast<const float *>(x)[base + i];
-        else
-            v = bf16_to_float(static_cast<const uint16_t *>(x)[base + i]);
-        if (!inverse && signs) v *= (float)signs[sbase + i];
-        buf[i] = v;
-    }
-    __syncthreads();
-    for (int s = 0; s < log2b; ++s) {
-        const int half = 1 << s;
-        for (int p = threadIdx.x; p < (block >> 1); p += blockDim.x) {
-            const int i = ((p >> s) << (s + 1)) | (p & (half - 1));
-            const float a = buf[i], c = buf[i + half];
-            buf[i] = a + c;
-            buf[i + half] = a - c;
+        float v[16];
+        const int64_t base = m * K + sbase + 16 * t;
+        if (live) {
+            if constexpr (XF32) {
+                const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + base);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 f = src[q];
+                    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+                }
+            } else {
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(x) + base);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u32x4_t d = src[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[8 * q + 2 * e] = bf16_to_float((uint16_t)(d[e] & 0xffffu));
+                        v[8 * q + 2 * e + 1] = bf16_to_float((uint16_t)(d[e] >> 16));
+                    }
+                }
+            }
+            if (!inverse && signs) {
+                const u32x4_t d = *reinterpret_cast<const u32x4_t *>(signs + sbase + 16 * t);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] *= (float)(int8_t)((d[r >> 2] >> (8 * (r & 3))) & 0xffu);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] = 0.0f;
         }
-        __syncthreads();
+        // pass 0: register bits = index bits 0..3
+        butterfly_bits(v, 0, 4);
+        int rb = 0;
+        for (int lo = 4; lo < L; lo += 4) {
+            const int nrb = (lo + 4 <= L) ? lo : L - 4;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lb[fwht_pad(fwht_index(t, r, rb))] = v[r];
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] = lb[fwht_pad(fwht_index(t, r, nrb))];
+            __syncthreads();
+            butterfly_bits(v, lo - nrb, L - nrb < 4 ? L - nrb : 4);
+            rb = nrb;
+        }
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = fwht_index(t, r, rb);
+                float o = v[r] * norm;
+                if (inverse && signs) o *= (float)signs[sbase + i];
+                y[m * K + sbase + i] = o;
+            }
+        }
     }
-    for (int i = threadIdx.x; i < block; i += blockDim.x) {
-        float v = buf[i] * norm;
-        if (inverse && signs) v *= (float)signs[sbase + i];
-        y[base + i] = v;
-    }
-    __syncthreads();  // the next row reuses buf
+}
+
+// Blocks of fewer than 16 elements: one thread per block, in registers.
+template <bool XF32>
+__global__ __launch_bounds__(256) void fwht_small_kernel(
+    const void *__restrict__ x, const int8_t *__restrict__ signs, int64_t M, int64_t K, int L,
+    int inverse, float *y, float norm)
+{
+    const int b = 1 << L;
+    const int64_t total = M * (K >> L);
+    for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < total;
+         blk += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t base = blk << L;
+        const int64_t sb = base % K;
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            v[r] = 0.0f;
+            if (r < b) {
+                v[r] = XF32 ? static_cast<const float *>(x)[base + r]
+                            : bf16_to_float(static_cast<const uint16_t *>(x)[base + r]);
+                if (!inverse && signs) v[r] *= (float)signs[sb + r];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if (j >= L) continue;
+            const int h = 1 << j;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if ((r & h) || r >= b) continue;
+                const float a = v[r], c = v[r | h];
+                v[r] = a + c;
+                v[r | h] = a - c;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (r < b) {
+                float o = v[r] * norm;
+                if (inverse && signs) o *= (float)signs[sb + r];
+                y[base + r] = o;
+            }
+        }
     }
 }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-// Largest LDS request made so far per (kernel, device); raising the limit
-// above the 64 KiB default needs hipFuncSetAttribute once.
+// Raising a kernel's dynamic LDS limit above the 64 KiB default needs
+// hipFuncSetAttribute once per (kernel, device).
 template <class Kernel>
 int ensure_lds(Kernel kernel, size_t bytes)
 {
-    static std::atomic<size_t> granted[64];
+    static std::atomic<int> granted[64];
     if (bytes <= 65536) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (granted[dev].load(std::memory_order_relaxed) >= bytes) return 0;
+    if (granted[dev].load(std::memory_order_relaxed)) return 0;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
     if (e != hipSuccess) return (int)e;
-    granted[dev].store(kMaxLds, std::memory_order_relaxed);
+    granted[dev].store(1, std::memory_order_relaxed);
     return 0;
 }
 
 struct GemvPlan {
-    int waves;
-    int wave_groups;
+    int tpw, wk, wt;
+    int64_t wgs;
     size_t lds;
 };
 
-// Waves per workgroup: enough waves in flight to cover HBM latency and at
-// least two 256-K blocks per wave.  LDS holds every wave's staged
-// activations plus the reduction area.
-inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx, int tpw)
+// Tiles per wave and the split of a workgroup's waves between tiles (wt)
+// and K (wk).  Large N: waves take different tiles over all of K (no
+// reduction; the staged activations serve wt * TPW tiles).  Small N: waves
+// split K of the same tiles so that there are enough waves in flight (about
+// 2048 in total), each with at least two 256-K blocks.
+inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
 {
-    const int64_t tiles = (N + kTileN * tpw - 1) / (kTileN * tpw);
-    const int G = (int)(K / kGroup);
-    int waves = 1;
-    while (waves < 8 && tiles * waves < 2048 && G >= 4 * waves) waves *= 2;
+    const int64_t tiles = (N + kTileN - 1) / kTileN;
+    const int nblk = (int)((K / kGroup + 1) / 2);
     GemvPlan pl;
-    pl.waves = waves;
-    pl.wave_groups = (G + waves - 1) / waves;
-    pl.lds = (size_t)waves * pl.wave_groups * kGroup * mx * 2 +
-             (size_t)waves * tpw * mx * kTileN * sizeof(float);
+    pl.tpw = (mx <= 4 && tiles >= 4096) ? 2 : ((tiles + 1) / 2 >= 512 ? 2 : 1);
+    const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
+    pl.wt = 1;
+    while (pl.wt < 4 && tile_groups / (pl.wt * 2) >= 1024) pl.wt *= 2;
+    pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
+    pl.wk = 1;
+    while (pl.wt * pl.wk < 8 && pl.wgs * pl.wt * pl.wk < 2048 && nblk >= 4 * pl.wk) pl.wk *= 2;
+    const int waves = pl.wt * pl.wk;
+    pl.lds = (size_t)K * mx * 2 + (size_t)waves * pl.tpw * mx * kTileN * sizeof(float);
     return pl;
 }
 
-template <int MX, bool XF32, int TPW, int PF>
-int launch_gemv_t(const void *x, int M, int64_t K, const uint32_t *codes, const uint16_t *scales,
-                  int64_t N, void *y, bool y_bf16, hipStream_t stream)
+template <int MX, bool XF32, int TPW>
+int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
-    const GemvPlan pl = plan_gemv(N, K, MX, TPW);
-    auto kernel = gemv_kernel<MX, XF32, TPW, PF>;
+    auto kernel = (a.K / kGroup) % 2 == 0 ? gemv_kernel<MX, XF32, TPW, true>
+                                          : gemv_kernel<MX, XF32, TPW, false>;
     int rc = ensure_lds(kernel, pl.lds);
     if (rc) return rc;
-    const int64_t tiles = (N + kTileN * TPW - 1) / (kTileN * TPW);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * pl.waves), pl.lds, stream, x, M, K,
-                       codes, scales, N, y, (int)y_bf16, pl.waves, pl.wave_groups);
+    a.wk = pl.wk;
+    a.wt = pl.wt;
+    a.bq = a.nblk / pl.wk;
+    a.br = a.nblk % pl.wk;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * pl.wk * pl.wt), pl.lds, stream, a);
     return (int)hipGetLastError();
 }
 
-template <bool XF32>
-int launch_gemv_x(const void *x, int M, int64_t K, const uint32_t *codes, const uint16_t *scales,
-                  int64_t N, void *y, bool y_bf16, hipStream_t stream)
+template <int MX, bool XF32>
+int launch_gemv_mx(const GemvArgs &a, const GemvPlan &pl, hipStream_t stream)
 {
-    const int Mx = XF32 ? 2 * M : M;
-    if (Mx <= 1) return launch_gemv_t<1, XF32, 1, 4>(x, M, K, codes, scales, N, y, y_bf16, stream);
-    if (Mx <= 2) return launch_gemv_t<2, XF32, 1, 4>(x, M, K, codes, scales, N, y, y_bf16, stream);
-    if (Mx <= 4) return launch_gemv_t<4, XF32, 1, 4>(x, M, K, codes, scales, N, y, y_bf16, stream);
-    if (Mx <= 8) return launch_gemv_t<8, XF32, 2, 2>(x, M, K, codes, scales, N, y, y_bf16, stream);
-    if (Mx <= 16) return launch_gemv_t<16, XF32, 4, 1>(x, M, K, codes, scales, N, y, y_bf16, stream);
-    return (int)hipErrorInvalidValue;
+    if (pl.tpw == 2) return launch_gemv_t<MX, XF32, 2>(a, pl, stream);
+    return launch_gemv_t<MX, XF32, 1>(a, pl, stream);
 }
 
-// Rows of x one launch can take: every staged row costs 2 bytes per K of
-// LDS (two rows for binary32 input); larger M runs as several launches.
+template <bool XF32>
+int launch_gemv_x(GemvArgs a, hipStream_t stream)
+{
+    const int Mx = XF32 ? 2 * a.M : a.M;
+    const int mx = Mx <= 1 ? 1 : Mx <= 2 ? 2 : Mx <= 4 ? 4 : Mx <= 8 ? 8 : 16;
+    const GemvPlan pl = plan_gemv(a.N, a.K, mx);
+    switch (mx) {
+    case 1: return launch_gemv_mx<1, XF32>(a, pl, stream);
+    case 2: return launch_gemv_mx<2, XF32>(a, pl, stream);
+    case 4: return launch_gemv_mx<4, XF32>(a, pl, stream);
+    case 8: return launch_gemv_mx<8, XF32>(a, pl, stream);
+    default: return launch_gemv_mx<16, XF32>(a, pl, stream);
+    }
+}
+
+// Rows of x one launch takes: the staged activations (2 bytes per K per A
+// row, two A rows per binary32 input row) must fit in LDS; larger M runs as
+// several launches over the same weights.
 inline int gemv_rows_per_launch(int64_t N, int64_t K, bool x_f32)
 {
     const int per = x_f32 ? 2 : 1;
-    for (int rows = 16 / per; rows > 1; rows /= 2) {
-        int mx = rows * per;
-        int tpw = mx <= 4 ? 1 : (mx <= 8 ? 2 : 4);
-        if (plan_gemv(N, K, mx, tpw).lds <= kMaxLds) return rows;
-    }
+    for (int rows = 16 / per; rows > 1; rows /= 2)
+        if (plan_gemv(N, K, rows * per).lds <= kMaxLds) return rows;
     return 1;
 }
 
@@ -488,11 +740,18 @@ int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *cod
     const int step = gemv_rows_per_launch(N, K, x_f32);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += step) {
-        const int mm = (M - m0) < step ? (M - m0) : step;
-        const void *xm = static_cast<const char *>(x) + (size_t)m0 * K * xsz;
-        void *ym = static_cast<char *>(y) + (size_t)m0 * N * ysz;
-        int rc = x_f32 ? launch_gemv_x<true>(xm, mm, K, codes, scales, N, ym, y_bf16, st)
-                       : launch_gemv_x<false>(xm, mm, K, codes, scales, N, ym, y_bf16, st);
+        GemvArgs a;
+        a.M = (M - m0) < step ? (M - m0) : step;
+        a.x = static_cast<const char *>(x) + (size_t)m0 * K * xsz;
+        a.y = static_cast<char *>(y) + (size_t)m0 * N * ysz;
+        a.codes = codes;
+        a.scales = scales;
+        a.N = N;
+        a.K = (int)K;
+        a.nblk = (int)((K / kGroup + 1) / 2);
+        a.bq = a.br = 0;
+        a.y_bf16 = y_bf16 ? 1 : 0;
+        int rc = x_f32 ? launch_gemv_x<true>(a, st) : launch_gemv_x<false>(a, st);
         if (rc) return rc;
     }
     return 0;
@@ -502,17 +761,37 @@ int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64
                 bool inverse, float *y, void *stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int log2b = 0;
-    while ((1 << log2b) < block) ++log2b;
+    int L = 0;
+    while ((1 << L) < block) ++L;
     const float norm = (float)(1.0 / __builtin_sqrt((double)block));
-    const int threads = block >= 512 ? 256 : (block >= 128 ? block / 2 : 64);
-    dim3 grid((unsigned)(K / block), (unsigned)(M < 65535 ? M : 65535));
+    const unsigned rows = (unsigned)(M < 65535 ? M : 65535);
+    if (L < 4) {
+        const int64_t total = M * (K >> L);
+        const unsigned grid = (unsigned)((total + 255) / 256 < 65535 * 16 ? (total + 255) / 256 : 65535 * 16);
+        if (x_f32)
+            hipLaunchKernelGGL(fwht_small_kernel<true>, dim3(grid), dim3(256), 0, st, x, signs, M, K, L,
+                               (int)inverse, y, norm);
+        else
+            hipLaunchKernelGGL(fwht_small_kernel<false>, dim3(grid), dim3(256), 0, st, x, signs, M, K, L,
+                               (int)inverse, y, norm);
+        return (int)hipGetLastError();
+    }
+    const int tpb = block / 16;
+    const int64_t blocks_per_row = K / block;
+    int bpw = 256 / tpb;
+    if (bpw > blocks_per_row) bpw = (int)blocks_per_row;
+    if (bpw < 1) bpw = 1;
+    const unsigned threads = (unsigned)(((tpb * bpw + 63) / 64) * 64);
+    // every thread, including padding threads past bpw blocks, owns an LDS
+    // block region (padding threads load nothing and store nothing)
+    const size_t lds = (size_t)(threads / tpb) * (block + block / 16) * sizeof(float);
+    dim3 grid((unsigned)((blocks_per_row + bpw - 1) / bpw), rows);
     if (x_f32)
-        hipLaunchKernelGGL(fwht_kernel<true>, grid, dim3(threads), block * sizeof(float), st, x, signs, M,
-                           K, block, log2b, (int)inverse, y, norm);
+        hipLaunchKernelGGL(fwht16_kernel<true>, grid, dim3(threads), lds, st, x, signs, M, K, L, bpw,
+                           (int)inverse, y, norm);
     else
-        hipLaunchKernelGGL(fwht_kernel<false>, grid, dim3(threads), block * sizeof(float), st, x, signs, M,
-                           K, block, log2b, (int)inverse, y, norm);
+        hipLaunchKernelGGL(fwht16_kernel<false>, grid, dim3(threads), lds, st, x, signs, M, K, L, bpw,
+                           (int)inverse, y, norm);
     return (int)hipGetLastError();
 }
 
