@@ -50,6 +50,12 @@ def gemv_bytes(M, K, N, x_bytes):
     return N * K // 4 + 2 * N * K // 128 + M * K * x_bytes + M * N * 4
 
 
+def rotated_step_bytes(w):
+    """Algorithmic HBM bytes of one rotated decode step: packed codes, FP16
+    scales, the bfloat16 activation row, the int8 signs and the FP32 output."""
+    return (w.N * w.K // 4 + 2 * w.N * w.K // 128 + w.M * w.K * 2 + w.K + w.M * w.N * 4)
+
+
 def make_pool(tern, torch, t, s, nbytes_each):
     codes, s2 = tern.tern_pack(t, s)
     c0, s0 = tern.to_device(codes, s2)
@@ -103,7 +109,13 @@ def bench_rotated(args, tern, torch, synth):
     w, host, pool, xd, dd, xr, y = rotated_step_setup(tern, torch, synth)
     P = len(pool)
 
+    # one step = sign flip + rotation + GEMV, fused in one kernel launch
     def step(i):
+        c, s = pool[i % P]
+        tern.tern_rotate_gemv(xd, dd, w.rotate_block, c, s, out=y)
+
+    # the same path as two launches (transform, then GEMV), for reference
+    def two_launch_step(i):
         c, s = pool[i % P]
         tern.tern_fwht(xd, dd, w.rotate_block, out=xr)
         tern.tern_gemv(xr, c, s, out=y)
@@ -123,8 +135,10 @@ def bench_rotated(args, tern, torch, synth):
     torch.cuda.synchronize()
     step_ms, g = time_graph(torch, step, args.steps)
     ms_per_step = step_ms / args.steps
+    two_ms, _ = time_graph(torch, two_launch_step, args.steps)
     gemv_ms, _ = time_graph(torch, gemv_only, args.steps)
     fwht_ms, _ = time_graph(torch, fwht_only, args.steps)
+    kernel_us = 1e3 * ms_per_step   # the step is one kernel
     gemv_us = 1e3 * gemv_ms / args.steps
     fwht_us = 1e3 * fwht_ms / args.steps
 
@@ -137,17 +151,20 @@ def bench_rotated(args, tern, torch, synth):
     torch.cuda.synchronize()
     assert torch.equal(y, y_eager), "graph replay differs from eager execution"
 
-    gb = gemv_bytes(w.M, w.K, w.N, 4)
-    fwht_b = w.M * w.K * 2 + w.K + w.M * w.K * 4
-    step_bytes = gb + fwht_b
+    # algorithmic bytes of the fused step: codes + scales + bf16 x + signs + y
+    step_bytes = rotated_step_bytes(w)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = gb / (gemv_us * 1e-6) / 1e9
+    achieved = step_bytes / (kernel_us * 1e-6) / 1e9
     res = {
         "value": value,
         "ms_per_step": ms_per_step,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None},
-        "detail": {"gemv_us": gemv_us, "fwht_us": fwht_us, "gemv_bytes": gb, "step_bytes": step_bytes,
+        "detail": {"kernel": "gemv_kernel<2, true, TPW, true, 1> (fused rotation + GEMV)",
+                   "kernel_us": kernel_us, "step_bytes": step_bytes,
+                   "two_launch_step_us": 1e3 * two_ms / args.steps,
+                   "gemv_only_us": gemv_us, "gemv_only_GBps": gemv_bytes(w.M, w.K, w.N, 4) / (gemv_us * 1e-6) / 1e9,
+                   "fwht_only_us": fwht_us,
                    "pool_copies": P, "pool_bytes": P * (tern.tern_codes_bytes(w.N, w.K) +
                                                         tern.tern_scales_bytes(w.N, w.K))},
     }
@@ -170,7 +187,7 @@ def cpu_baseline(w, host, min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    step_bytes = gemv_bytes(w.M, w.K, w.N, 4) + w.M * w.K * 2 + w.K + w.M * w.K * 4
+    step_bytes = rotated_step_bytes(w)
     return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full rotated decode steps (FP64 explicit-Hadamard rotation + "
                       f"naive FP64 matmul over all {w.N} rows), {el:.1f} s, single thread"}

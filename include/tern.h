@@ -150,6 +150,25 @@ tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K,
                       const uint32_t *codes, const uint16_t *scales, int64_t N,
                       void *y, int ydt, void *stream);
 
+/* Rotated decode in one launch: y = (H_b D x / sqrt(b)) (s_g t)^T, i.e. the
+ * signed normalized Walsh-Hadamard transform of tern_fwht (forward, blocks
+ * of b along K) followed by the tern_gemv matmul on the rotated binary32
+ * activations.  The rotation is the run-time half of the one the
+ * "Ternary-Bonsai-2-9B-2bit" article (section 3) folds into the stored
+ * weights; every workgroup applies it to x in LDS while the code stream is
+ * already in flight, so the rotated activations never go to memory.
+ * x: [M][K] TERN_F32 or TERN_BF16, 16-byte aligned; signs: int8 [K] of +-1
+ * (16-byte aligned) or NULL; block: a power of two in [16, 4096] with
+ * K % block == 0; M <= 16; codes, scales, y, ydt as tern_gemv.
+ * Accuracy: within tern_gemv's bound for the exact rotation plus
+ * sum_k |s_g t| |x'_k - exact x'_k| (the rotation is done in binary32).
+ * Errors: as tern_gemv; TERN_EUNSUPPORTED when the staged activations of
+ * one workgroup (about 8.25 * M * K bytes) exceed LDS -- use tern_fwht then
+ * tern_gemv instead. */
+tern_status tern_rotate_gemv(const void *x, int xdt, const int8_t *signs, int64_t block, int64_t M,
+                             int64_t K, const uint32_t *codes, const uint16_t *scales, int64_t N,
+                             void *y, int ydt, void *stream);
+
 /* Bytes of device workspace tern_gemm needs for these sizes (may be 0). */
 size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

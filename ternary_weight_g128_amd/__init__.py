@@ -26,7 +26,7 @@ TERN_FWHT_MAX_BLOCK = 4096
 EXPORTED = [
     "tern_abi_version", "tern_status_str", "tern_last_error", "tern_codes_bytes",
     "tern_scales_bytes", "tern_pack", "tern_pack_f32", "tern_unpack", "tern_dequant_f32",
-    "tern_fwht", "tern_gemv", "tern_gemm_workspace_bytes", "tern_gemm",
+    "tern_fwht", "tern_gemv", "tern_rotate_gemv", "tern_gemm_workspace_bytes", "tern_gemm",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -52,6 +52,7 @@ _lib.tern_unpack.argtypes = [_P, _I64, _I64, _P]
 _lib.tern_dequant_f32.argtypes = [_P, _P, _I64, _I64, _P]
 _lib.tern_fwht.argtypes = [_P, _I, _P, _I64, _I64, _I64, _I, _P, _P]
 _lib.tern_gemv.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
+_lib.tern_rotate_gemv.argtypes = [_P, _I, _P, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P]
 _lib.tern_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 _lib.tern_gemm_workspace_bytes.restype = _SZ
 _lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
@@ -206,6 +207,21 @@ def tern_gemv(x, codes, scales, out=None, out_dtype=None, stream=None):
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
     _check(_lib.tern_gemv(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
                           _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv")
+    return out
+
+
+def tern_rotate_gemv(x, signs, block: int, codes, scales, out=None, out_dtype=None, stream=None):
+    """y = rot(x) (s_g t)^T in one launch, rot = signed normalized WHT over
+    blocks of `block` along K (forward).  x: [M, K] float32 or bfloat16,
+    M <= 16; signs int8 [K] or None."""
+    torch = _torch()
+    M, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    _check(_lib.tern_rotate_gemv(_dev_ptr(x), _dt(x), _dev_ptr(signs), block, M, K, _dev_ptr(codes),
+                                 _dev_ptr(scales), N, _dev_ptr(out), _dt(out), _stream_ptr(stream)),
+           "tern_rotate_gemv")
     return out
 
 

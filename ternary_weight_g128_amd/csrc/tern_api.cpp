@@ -82,6 +82,55 @@ tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K, const uint32
                          "tern_gemv");
 }
 
+tern_status tern_rotate_gemv(const void *x, int xdt, const int8_t *signs, int64_t block, int64_t M,
+                             int64_t K, const uint32_t *codes, const uint16_t *scales, int64_t N,
+                             void *y, int ydt, void *stream)
+{
+    tern_status st = check_matmul_args("tern_rotate_gemv", x, xdt, M, K, codes, scales, N, y);
+    if (st != TERN_OK) return st;
+    if (M > TERN_GEMV_MAX_M) {
+        set_error("tern_rotate_gemv: M must be at most 16");
+        return TERN_EINVAL;
+    }
+    if (block < 16 || block > TERN_FWHT_MAX_BLOCK || (block & (block - 1)) != 0) {
+        set_error("tern_rotate_gemv: block must be a power of two in [16, 4096]");
+        return TERN_EINVAL;
+    }
+    if (K % block != 0) {
+        set_error("tern_rotate_gemv: K must be a multiple of block");
+        return TERN_EINVAL;
+    }
+    if (ydt != TERN_F32 && ydt != TERN_BF16) {
+        set_error("tern_rotate_gemv: output dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (K == 0) {
+        set_error("tern_rotate_gemv: K must be positive");
+        return TERN_EINVAL;
+    }
+    if (signs && !aligned(signs, 16)) {
+        set_error("tern_rotate_gemv: signs must be 16-byte aligned");
+        return TERN_EINVAL;
+    }
+    if (!aligned(y, ydt == TERN_F32 ? 4 : 2)) {
+        set_error("tern_rotate_gemv: y not aligned to its dtype");
+        return TERN_EINVAL;
+    }
+    if (N > ((int64_t)1 << 31) - 64) {
+        set_error("tern_rotate_gemv: N too large");
+        return TERN_EINVAL;
+    }
+    if (tern::rotate_gemv_lds(M, N, K) > tern::max_lds_bytes()) {
+        set_error("tern_rotate_gemv: M * K too large for one workgroup's LDS; use tern_fwht then "
+                  "tern_gemv");
+        return TERN_EUNSUPPORTED;
+    }
+    return device_status(tern::launch_rotate_gemv(x, xdt == TERN_F32, signs, (int)block, (int)M, K,
+                                                  codes, scales, N, y, ydt == TERN_BF16, stream),
+                         "tern_rotate_gemv");
+}
+
 size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0 || K % TERN_GROUP) return 0;

@@ -18,6 +18,11 @@ void clear_error();
 // out of this header).
 int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *codes,
                 const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream);
+int launch_rotate_gemv(const void *x, bool x_f32, const int8_t *signs, int block, int M, int64_t K,
+                       const uint32_t *codes, const uint16_t *scales, int64_t N, void *y, bool y_bf16,
+                       void *stream);
+size_t rotate_gemv_lds(int64_t M, int64_t N, int64_t K);
+size_t max_lds_bytes();
 int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64_t K,
                 int block, bool inverse, float *y, void *stream);
 int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes,

@@ -76,6 +76,33 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b)
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Hadamard helpers (natural Sylvester order: a butterfly over every index
+// bit).  See the transform section below for the data layout.
+// Element index for thread t (within a block) and register index r when the
+// register bits start at bit rb.
+__device__ __forceinline__ int fwht_index(int t, int r, int rb)
+{
+    return (t & ((1 << rb) - 1)) | (r << rb) | ((t >> rb) << (rb + 4));
+}
+
+__device__ __forceinline__ int fwht_pad(int i) { return i + (i >> 4); }
+
+__device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_hi)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < j_lo || j >= j_hi) continue;
+        const int h = 1 << j;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (r & h) continue;
+            const float a = v[r], c = v[r | h];
+            v[r] = a + c;
+            v[r | h] = a - c;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // GEMV for M <= 16
 // ---------------------------------------------------------------------------
@@ -120,6 +147,9 @@ struct GemvArgs {
     int wt;       // waves of a workgroup that split tiles (wt * wk waves)
     int bq, br;   // blocks per K-wave: bq, plus one for the first br K-waves
     int y_bf16;
+    const int8_t *signs;  // rotated input: +-1 per K (or NULL)
+    int log2b;            // rotated input: Hadamard block 2^log2b (>= 16)
+    float norm;           // rotated input: 1/sqrt(block)
 };
 
 // One staging unit: the 16 activations of word wi (k = 16 wi .. 16 wi + 15)
@@ -129,10 +159,23 @@ struct XUnit {
     uint32_t v[XF32 ? 16 : 8];
 };
 
-template <bool XF32>
+template <bool XF32, bool IN_F32 = XF32>
 __device__ __forceinline__ void load_unit(XUnit<XF32> &u, const GemvArgs &a, int m, int wi)
 {
-    if constexpr (XF32) {
+    if constexpr (XF32 && !IN_F32) {
+        // bfloat16 input widened to binary32 words (rotated staging)
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.x) + (int64_t)m * a.K + 16 * wi);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            u32x4_t d = src[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u.v[8 * q + 2 * e] = d[e] << 16;
+                u.v[8 * q + 2 * e + 1] = d[e] & 0xffff0000u;
+            }
+        }
+    } else if constexpr (XF32) {
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
             static_cast<const float *>(a.x) + (int64_t)m * a.K + 16 * wi);
 #pragma unroll
@@ -203,19 +246,28 @@ __device__ __forceinline__ uint32_t quad_scale(uint32_t sq, int j)
     return __builtin_amdgcn_permlane16_swap(r2, r2, false, false)[1];
 }
 
-// PF == 4: the code ring holds one quad of four 256-K blocks.  For MX <= 4
+// PF == 4: the code ring holds one quad of four 256-K blocks (refilled two
+// blocks ahead).  For MX <= 4
 // every live output row sits in lane group 0, so the scales of a quad come
 // from one load per lane (lane group g loads block g's scale pair) and are
 // redistributed with cross-row swaps; for larger MX each lane loads its
 // row's pair per block.
-template <int MX, bool XF32, int TPW, bool SC4>
+// ROT = 0: x is the activation (binary32 if XF32, else bfloat16).
+// ROT = 1 / 2: x (bfloat16 / binary32) is rotated first: the workgroup
+// computes d .* x in a padded binary32 LDS scratch, applies the Hadamard
+// butterflies there (same register-radix-16 passes as the stand-alone
+// transform, while the code stream is already in flight), scales by
+// 1/sqrt(b) and stages the result as hi/lo bfloat16 rows (XF32 == true).
+template <int MX, bool XF32, int TPW, bool SC4, int ROT = 0, int ROTL = 0>
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 {
+    static_assert(ROT == 0 || XF32, "rotated activations are staged as hi/lo rows");
     constexpr int PF = 4;
+    constexpr int kDist = 2;
     constexpr bool kQuadScales = MX <= 4;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int kRowsOut = (MX < 4) ? MX : 4;  // accumulator rows per lane that can be live
-    constexpr int kUB = XF32 ? 2 : 4;            // staging units per thread per batch
+    constexpr int kUB = ROT ? 1 : (XF32 ? 2 : 4);  // staging units per thread per batch
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
@@ -253,7 +305,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     // thread a staging unit; the loads below are unconditional so that the
     // compiler can count outstanding loads exactly.
     __bf16 *lds_x = reinterpret_cast<__bf16 *>(smem);
-    float *red = reinterpret_cast<float *>(smem + (size_t)a.K * MX * 2);
+    const int rowpad = a.K + (a.K >> 4);  // padded row of the rotation scratch
+    float *rot = reinterpret_cast<float *>(smem + (size_t)a.K * MX * 2);
+    float *red = rot + (ROT ? (size_t)a.M * rowpad : 0);
 
     // 1. activation loads for the first staging batch go out first, so that
     //    waiting for them does not wait for the code stream issued next.
@@ -262,12 +316,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     const int wpr = a.K / 16;  // words (units) per activation row
     const int units = a.M * wpr;
     const int nthreads = 64 * waves;
+    constexpr bool kInF32 = ROT ? (ROT == 2) : XF32;
     XUnit<XF32> xu[kUB];
+    u32x4_t du[kUB];  // signs of the unit (rotation)
 #pragma unroll
     for (int i = 0; i < kUB; ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
-        load_unit<XF32>(xu[i], a, u / wpr, u % wpr);
+        load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
+        if constexpr (ROT != 0)
+            du[i] = a.signs ? *reinterpret_cast<const u32x4_t *>(a.signs + 16 * (u % wpr))
+                            : u32x4_t{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
     }
 
     // 2. code stream: one quad ahead
@@ -312,32 +371,105 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             for (int tp = 0; tp < TPW; ++tp) squad[tp] = scale_pair(tp, gb, two);
         }
     };
+    // The ring has PF slots (one quad, the unit of the scale loads) but is
+    // refilled only kDist blocks ahead: waves start computing as soon as
+    // their first blocks land while the other waves keep HBM busy.
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load_block(p, p);
+    for (int p = 0; p < kDist; ++p) load_block(p, p);
     load_quad_scales(0);
 
     // 3. stage the activations of all of K (shared by the waves)
+    auto put = [&](const XUnit<XF32> &xv, const u32x4_t &dv, int u) {
+        const int m = u / wpr, wi = u % wpr;
+        if constexpr (ROT == 0) {
+            store_unit<MX, XF32>(lds_x, xv, m, wi);
+        } else {
+            // a unit is 16 consecutive elements: exactly one group of the
+            // first butterfly pass (index bits 0..3), done here in registers
+            float v[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float sg = (float)(int8_t)((dv[e >> 2] >> (8 * (e & 3))) & 0xffu);
+                v[e] = __builtin_bit_cast(float, xv.v[e]) * sg;
+            }
+            butterfly_bits(v, 0, 4);
+            float *row = rot + (size_t)m * rowpad + 17 * wi;  // pad(16 wi + e) = 17 wi + e
+#pragma unroll
+            for (int e = 0; e < 16; ++e) row[e] = v[e];
+        }
+    };
 #pragma unroll
     for (int i = 0; i < kUB; ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
-        store_unit<MX, XF32>(lds_x, xu[i], u / wpr, u % wpr);
+        put(xu[i], du[i], u);
     }
     for (int u0 = kUB * nthreads; u0 < units; u0 += kUB * nthreads) {
 #pragma unroll
         for (int i = 0; i < kUB; ++i) {
             int u = u0 + threadIdx.x + i * nthreads;
             u = u < units ? u : units - 1;
-            load_unit<XF32>(xu[i], a, u / wpr, u % wpr);
+            load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
+            if constexpr (ROT != 0)
+                du[i] = a.signs ? *reinterpret_cast<const u32x4_t *>(a.signs + 16 * (u % wpr))
+                                : u32x4_t{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
         }
 #pragma unroll
         for (int i = 0; i < kUB; ++i) {
             int u = u0 + threadIdx.x + i * nthreads;
             u = u < units ? u : units - 1;
-            store_unit<MX, XF32>(lds_x, xu[i], u / wpr, u % wpr);
+            put(xu[i], du[i], u);
         }
     }
     __syncthreads();
+    if constexpr (ROT != 0) {
+        // Hadamard butterflies over each block of 2^log2b along K, four
+        // index bits per pass; a group is 16 values that differ only in the
+        // pass's register bits (see fwht_index).
+        const int L = ROTL ? ROTL : a.log2b;       // compile-time for 4096-point blocks
+        const int tpb = 1 << (L - 4);              // groups per block per pass
+        const int ngroups_all = a.M * (a.K >> 4);
+        // index bits 0..3 were done at staging; the later passes
+        for (int lo = 4; lo < L; lo += 4) {
+            const int nrb = (lo + 4 <= L) ? lo : L - 4;
+            const int j_lo = lo - nrb, j_hi = (L - nrb < 4) ? L - nrb : 4;
+            // with register bits at nrb >= 4 the padded index of value r is
+            // base + r * (2^nrb + 2^(nrb - 4)): the register bits carry no
+            // part of the low four index bits
+            const int cstride = (1 << nrb) + (1 << (nrb - 4));
+            for (int q = threadIdx.x; q < ngroups_all; q += nthreads) {
+                const int m = a.M == 1 ? 0 : q / wpr, rest = q - m * wpr;
+                const int blk = rest >> (L - 4), t = rest & (tpb - 1);
+                float *base = rot + (size_t)m * rowpad + fwht_pad((blk << L) + fwht_index(t, 0, nrb));
+                float v[16];
+                if (nrb >= 4) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) v[r] = base[r * cstride];
+                    butterfly_bits(v, j_lo, j_hi);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) base[r * cstride] = v[r];
+                } else {
+                    float *row = rot + (size_t)m * rowpad;
+                    const int kb = blk << L;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) v[r] = row[fwht_pad(kb + fwht_index(t, r, nrb))];
+                    butterfly_bits(v, j_lo, j_hi);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) row[fwht_pad(kb + fwht_index(t, r, nrb))] = v[r];
+                }
+            }
+            __syncthreads();
+        }
+        for (int u = threadIdx.x; u < units; u += nthreads) {
+            const int m = u / wpr, wi = u % wpr;
+            const float *row = rot + (size_t)m * rowpad + 17 * wi;
+            XUnit<XF32> xv;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) xv.v[e] = __builtin_bit_cast(uint32_t, row[e] * a.norm);
+            store_unit<MX, XF32>(lds_x, xv, m, wi);
+        }
+        __syncthreads();
+    }
 
     // 4. stream the codes
     float yacc[TPW][kRowsOut];
@@ -385,7 +517,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             sc[tp][0] = half_to_float((uint16_t)(pair & 0xffffu));
             sc[tp][1] = two ? half_to_float((uint16_t)(pair >> 16)) : 0.0f;
         }
-        if (refill) load_block(b + PF, p);
+        if (refill) load_block(b + kDist, (p + kDist) % PF);
         f32x4_t acc0[TPW], acc1[TPW];
 #pragma unroll
         for (int tp = 0; tp < TPW; ++tp) {
@@ -422,7 +554,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-        if (nfull + p < nblocks) process(nfull + p, p, squad, false);
+        if (nfull + p < nblocks) process(nfull + p, p, squad, true);
 
     // 5. combine the K-waves' partial sums in a fixed order and store
     auto store = [&](int m, int64_t n, float sum) {
@@ -488,31 +620,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 // i + i / 16, which keeps the strided transposes free of bank conflicts.
 // binary32 throughout; the 1/sqrt(b) factor is applied once at the end (a
 // power of two, so exact, when L is even).
-
-// Element index for thread t (within a block) and register index r when the
-// register bits start at bit rb.
-__device__ __forceinline__ int fwht_index(int t, int r, int rb)
-{
-    return (t & ((1 << rb) - 1)) | (r << rb) | ((t >> rb) << (rb + 4));
-}
-
-__device__ __forceinline__ int fwht_pad(int i) { return i + (i >> 4); }
-
-__device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_hi)
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < j_lo || j >= j_hi) continue;
-        const int h = 1 << j;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (r & h) continue;
-            const float a = v[r], c = v[r | h];
-            v[r] = a + c;
-            v[r | h] = a - c;
-        }
-    }
-}
 
 template <bool XF32>
 __global__ __launch_bounds__(256) void fwht16_kernel(
@@ -716,6 +823,67 @@ int launch_gemv_x(GemvArgs a, hipStream_t stream)
     }
 }
 
+inline int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+// Fused rotation: every workgroup transforms the activations once, so use
+// about one workgroup per CU (up to four tiles per wave) and split K over
+// up to four waves (all 256 threads then take part in the butterflies).
+inline GemvPlan plan_rotate_gemv(int64_t N, int64_t K, int M, int mx)
+{
+    const int64_t tiles = (N + kTileN - 1) / kTileN;
+    const int nblk = (int)((K / kGroup + 1) / 2);
+    const int cus = device_cus();
+    GemvPlan pl;
+    int64_t t = (tiles + cus - 1) / cus;
+    pl.tpw = (int)(t < 1 ? 1 : (t > 4 ? 4 : t));
+    pl.wt = 1;
+    pl.wgs = (tiles + pl.tpw - 1) / pl.tpw;
+    pl.wk = 1;
+    while (pl.wk < 4 && nblk >= 2 * (pl.wk * 2)) pl.wk *= 2;
+    pl.lds = (size_t)K * mx * 2 + (size_t)M * (K + K / 16) * 4 +
+             (size_t)pl.wk * pl.tpw * mx * kTileN * sizeof(float);
+    return pl;
+}
+
+template <int MX, int ROT, int ROTL>
+void (*rotate_kernel(int tpw, bool sc4))(GemvArgs)
+{
+    switch (tpw) {
+    case 1: return sc4 ? gemv_kernel<MX, true, 1, true, ROT, ROTL> : gemv_kernel<MX, true, 1, false, ROT, ROTL>;
+    case 2: return sc4 ? gemv_kernel<MX, true, 2, true, ROT, ROTL> : gemv_kernel<MX, true, 2, false, ROT, ROTL>;
+    case 3: return sc4 ? gemv_kernel<MX, true, 3, true, ROT, ROTL> : gemv_kernel<MX, true, 3, false, ROT, ROTL>;
+    default: return sc4 ? gemv_kernel<MX, true, 4, true, ROT, ROTL> : gemv_kernel<MX, true, 4, false, ROT, ROTL>;
+    }
+}
+
+template <int MX, int ROT>
+int launch_rotate_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
+{
+    const bool sc4 = (a.K / kGroup) % 2 == 0;
+    void (*kernel)(GemvArgs) = a.log2b == 12 ? rotate_kernel<MX, ROT, 12>(pl.tpw, sc4)
+                                             : rotate_kernel<MX, ROT, 0>(pl.tpw, sc4);
+    int rc = ensure_lds(kernel, pl.lds);
+    if (rc) return rc;
+    a.wk = pl.wk;
+    a.wt = pl.wt;
+    a.bq = a.nblk / pl.wk;
+    a.br = a.nblk % pl.wk;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * pl.wk), pl.lds, stream, a);
+    return (int)hipGetLastError();
+}
+
 // Rows of x one launch takes: the staged activations (2 bytes per K per A
 // row, two A rows per binary32 input row) must fit in LDS; larger M runs as
 // several launches over the same weights.
@@ -751,7 +919,70 @@ int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *cod
         a.nblk = (int)((K / kGroup + 1) / 2);
         a.bq = a.br = 0;
         a.y_bf16 = y_bf16 ? 1 : 0;
+        a.signs = nullptr;
+        a.log2b = 0;
+        a.norm = 1.0f;
         int rc = x_f32 ? launch_gemv_x<true>(a, st) : launch_gemv_x<false>(a, st);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+// Rotated activations are staged as hi/lo rows, two A rows per input row,
+// so one launch takes at most 8 rows of x; larger M runs as several.
+constexpr int kRotRowsPerLaunch = 8;
+
+size_t rotate_gemv_lds(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t mm = M < kRotRowsPerLaunch ? M : kRotRowsPerLaunch;
+    const int mx = 2 * mm <= 2 ? 2 : 2 * mm <= 4 ? 4 : 2 * mm <= 8 ? 8 : 16;
+    return plan_rotate_gemv(N, K, (int)mm, mx).lds;
+}
+
+size_t max_lds_bytes() { return kMaxLds; }
+
+static int launch_rotate_rows(const void *x, bool x_f32, const int8_t *signs, int block, int M, int64_t K,
+                              const uint32_t *codes, const uint16_t *scales, int64_t N, void *y,
+                              bool y_bf16, hipStream_t st)
+{
+    GemvArgs a;
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.y = y;
+    a.N = N;
+    a.K = (int)K;
+    a.M = M;
+    a.nblk = (int)((K / kGroup + 1) / 2);
+    a.wk = a.wt = 1;
+    a.bq = a.br = 0;
+    a.y_bf16 = y_bf16 ? 1 : 0;
+    a.signs = signs;
+    int L = 0;
+    while ((1 << L) < block) ++L;
+    a.log2b = L;
+    a.norm = (float)(1.0 / __builtin_sqrt((double)block));
+    const int mx = 2 * M <= 2 ? 2 : 2 * M <= 4 ? 4 : 2 * M <= 8 ? 8 : 16;
+    const GemvPlan pl = plan_rotate_gemv(N, K, M, mx);
+    switch (mx) {
+    case 2: return x_f32 ? launch_rotate_t<2, 2>(a, pl, st) : launch_rotate_t<2, 1>(a, pl, st);
+    case 4: return x_f32 ? launch_rotate_t<4, 2>(a, pl, st) : launch_rotate_t<4, 1>(a, pl, st);
+    case 8: return x_f32 ? launch_rotate_t<8, 2>(a, pl, st) : launch_rotate_t<8, 1>(a, pl, st);
+    default: return x_f32 ? launch_rotate_t<16, 2>(a, pl, st) : launch_rotate_t<16, 1>(a, pl, st);
+    }
+}
+
+int launch_rotate_gemv(const void *x, bool x_f32, const int8_t *signs, int block, int M, int64_t K,
+                       const uint32_t *codes, const uint16_t *scales, int64_t N, void *y, bool y_bf16,
+                       void *stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
+    for (int m0 = 0; m0 < M; m0 += kRotRowsPerLaunch) {
+        const int mm = (M - m0) < kRotRowsPerLaunch ? (M - m0) : kRotRowsPerLaunch;
+        int rc = launch_rotate_rows(static_cast<const char *>(x) + (size_t)m0 * K * xsz, x_f32, signs, block,
+                                    mm, K, codes, scales, N, static_cast<char *>(y) + (size_t)m0 * N * ysz,
+                                    y_bf16, st);
         if (rc) return rc;
     }
     return 0;

@@ -112,6 +112,20 @@ def test_fwht_empty_is_noop(tern):
     assert _fwht(tern, M=0, x=NULL, y=NULL) == 0
 
 
+def _rot(tern, x=A16, xdt=1, signs=NULL, block=4096, M=1, K=4096, codes=A16, scales=A16, N=16,
+         y=A16, ydt=0):
+    return tern.lib().tern_rotate_gemv(x, xdt, signs, block, M, K, codes, scales, N, y, ydt, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), 1), (dict(block=8192, K=8192), 1), (dict(block=1000), 1), (dict(K=6144), 1),
+    (dict(M=17), 1), (dict(xdt=4), 4), (dict(ydt=3), 4), (dict(signs=A2), 1), (dict(x=NULL), 1),
+    (dict(M=16, K=65536, block=4096), 4),   # staged activations exceed LDS
+])
+def test_rotate_gemv_rejects(tern, kw, status):
+    assert _rot(tern, **kw) == status
+
+
 def test_codec_rejects(tern):
     t = np.zeros((2, 128), dtype=np.int8)
     t[1, 5] = 2

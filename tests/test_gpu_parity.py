@@ -268,6 +268,62 @@ def test_rotated_decode_full_size(tern, oracle_lib):
 
 
 # ---------------------------------------------------------------------------
+# Fused rotation + GEMV (one launch)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N,block,xdt,signed", [
+    (1, 4096, 300, 4096, "bf16", True), (1, 4096, 777, 4096, "f32", True), (2, 8192, 100, 4096, "bf16", True),
+    (1, 1024, 64, 256, "bf16", False), (3, 2048, 50, 64, "f32", True), (4, 512, 33, 16, "bf16", True),
+    (1, 384, 40, 128, "f32", False), (8, 1024, 20, 1024, "bf16", True), (16, 256, 70, 32, "bf16", True),
+])
+def test_rotate_gemv_matches_oracle(tern, oracle_lib, M, K, N, block, xdt, signed):
+    seed = 3 * M + K + N + block
+    print(f"rotate gemv M={M} K={K} N={N} b={block} {xdt}", flush=True)
+    T = torch()
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = _x(seed, M, K, xdt)
+    d = synth.signs(seed, K) if signed else None
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = tern.tern_rotate_gemv(x_to_device(x), T.from_numpy(d).cuda() if signed else None, block,
+                              codes_d, scales_d)
+    T.cuda.synchronize()
+    x64 = x.astype(np.float64) if xdt == "f32" else oracle_lib.bf16_bits_to_f64(x)
+    xr = oracle_lib.fwht(x64, d, block)
+    codes_o = oracle_lib.encode(t)
+    y_ref, bound = oracle_lib.matmul(xr, codes_o, s, K)
+    # binary32 rotation error (rel L2 <= 1e-5 per row) propagates through
+    # sum |s t| |dx|; allow it on top of the matmul bound
+    wabs = np.abs(oracle_lib.dequant(codes_o, s, K))
+    rot_err = 1e-5 * np.linalg.norm(xr, axis=1, keepdims=True) * np.sqrt((wabs ** 2).sum(axis=1))[None, :]
+    assert_matmul_close(y_to_host(y), y_ref, bound + 1e4 * rot_err, what="rotate gemv")
+
+
+def test_rotate_gemv_full_size_matches_two_launch_path(tern, oracle_lib):
+    w = synth.ROTATED
+    seed = 606
+    print("rotated decode fused", flush=True)
+    rows = sampled_rows(w.N, 200, seed)
+    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, w.N, w.K, w.p_zero, rows)
+    T = torch()
+    x = synth.activations_bf16(seed, 1, w.K)
+    d = synth.signs(seed, w.K)
+    xd, dd = x_to_device(x), T.from_numpy(d).cuda()
+    y1 = tern.tern_rotate_gemv(xd, dd, w.rotate_block, codes_d, scales_d)
+    y1b = tern.tern_rotate_gemv(xd, dd, w.rotate_block, codes_d, scales_d)
+    y2 = tern.tern_gemv(tern.tern_fwht(xd, dd, w.rotate_block), codes_d, scales_d)
+    T.cuda.synchronize()
+    assert T.equal(y1, y1b)                      # deterministic
+    xr = oracle_lib.fwht(oracle_lib.bf16_bits_to_f64(x), d, w.rotate_block)
+    codes_o = oracle_lib.encode(t_rows)
+    y_ref, bound = oracle_lib.matmul(xr, codes_o, s_rows, w.K)
+    wabs = np.abs(oracle_lib.dequant(codes_o, s_rows, w.K))
+    rot_err = 1e-5 * np.linalg.norm(xr) * np.sqrt((wabs ** 2).sum(axis=1))[None, :]
+    for y in (y1, y2):
+        assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound + 1e4 * rot_err, what="fused vs oracle")
+
+
+# ---------------------------------------------------------------------------
 # GEMM (any M)
 # ---------------------------------------------------------------------------
 
