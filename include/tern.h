@@ -173,11 +173,15 @@ tern_status tern_rotate_gemv(const void *x, int xdt, const int8_t *signs, int64_
 size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Prefill-regime matmul, same definition as tern_gemv, any M >= 0 (tuned for
- * M >= 64): unpacked codes feed bf16 matrix-core (MFMA) tiles; accumulation
- * is binary32 per 128-K group, then scaled by s_g in binary32.
+ * M in the hundreds and up): unpacked codes feed bf16 matrix-core (MFMA)
+ * tiles as exact -2t operands; each accumulator is kept in units of its
+ * column's current group scale and rescaled in binary32 at every group
+ * boundary (one multiply per group), then multiplied by the last scale.
  * x: [M][K] TERN_BF16 only, 16-byte aligned; codes 16-byte aligned;
- * y: float [M][N]; workspace: device memory of at least
- * tern_gemm_workspace_bytes(M, N, K) bytes (NULL allowed when that is 0).
+ * K <= 4194176 (2^22 - 128); y: float [M][N]; workspace: device memory of
+ * at least tern_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned (NULL
+ * allowed when that is 0); it holds partial sums of output tiles that are
+ * split along K, and its contents on entry do not matter.
  * Accuracy as tern_gemv.  Errors: TERN_EINVAL, TERN_EUNSUPPORTED,
  * TERN_EDEVICE. */
 tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K,

@@ -10,19 +10,28 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtern.so")
 
-SOURCES = ["tern_kernels.hip", "tern_api.cpp", "tern_codec.cpp"]
+# (source, extra flags).  The GEMM keeps its MFMA accumulators in ordinary
+# VGPRs: it rescales them every 128-K group, and accumulator registers would
+# need a copy out and back for each rescale.
+SOURCES = [
+    ("tern_kernels.hip", []),
+    ("tern_gemm.hip", ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]),
+    ("tern_api.cpp", []),
+    ("tern_codec.cpp", []),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # Packed FP32 VALU instructions stay off: the compiler must not form them.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
+
+NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
 
 def hipcc() -> str:
@@ -30,20 +39,29 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libtern.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in proc.stderr.splitlines() if NOISE not in l)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtern.so (always recompiles)."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        _run([hipcc(), *HIPCC_FLAGS, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

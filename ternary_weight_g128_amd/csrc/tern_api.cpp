@@ -147,6 +147,10 @@ tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32
         set_error("tern_gemm: activations must be TERN_BF16");
         return TERN_EUNSUPPORTED;
     }
+    if (K > tern::gemm_max_k()) {
+        set_error("tern_gemm: K above " + std::to_string(tern::gemm_max_k()));
+        return TERN_EINVAL;
+    }
     if (M == 0 || N == 0) return TERN_OK;
     if (!aligned(y, 4)) {
         set_error("tern_gemm: y must be 4-byte aligned");

@@ -21,60 +21,16 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "tern_internal.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+#include "tern_device.h"
 
-constexpr int kGroup = 128;          // weights per scale
-constexpr int kWordsPerGroup = 8;    // 16 slots per uint32
-constexpr int kTileN = 16;           // output rows per MFMA tile
-constexpr unsigned kFlip = 0x55555555u;
-
-// Packed bfloat16 pair holding -2t for slot j (low half) and slot j + 8
-// (high half) of a flipped code word.
-__device__ __forceinline__ unsigned neg2t_pair(unsigned flipped, int j)
-{
-    u16x2_t v = __builtin_bit_cast(u16x2_t, flipped);
-    v = (v >> (unsigned short)(2 * j)) << (unsigned short)14;
-    return __builtin_bit_cast(unsigned, v);
-}
-
-// MFMA B operand (8 bf16) from half h (slots 4h..4h+3 and 4h+8..4h+11) of a
-// flipped word.  Element e corresponds to slot 4h + (e >> 1) + 8 (e & 1).
-__device__ __forceinline__ bf16x8_t weights_operand(unsigned flipped, int h)
-{
-    u32x4_t p;
-    p[0] = neg2t_pair(flipped, 4 * h + 0);
-    p[1] = neg2t_pair(flipped, 4 * h + 1);
-    p[2] = neg2t_pair(flipped, 4 * h + 2);
-    p[3] = neg2t_pair(flipped, 4 * h + 3);
-    return __builtin_bit_cast(bf16x8_t, p);
-}
-
-__device__ __forceinline__ float half_to_float(uint16_t h)
-{
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ __forceinline__ uint16_t float_to_bf16_rne(float f)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_to_float(uint16_t b)
-{
-    return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
 
 // Hadamard helpers (natural Sylvester order: a butterfly over every index
 // bit).  See the transform section below for the data layout.
@@ -739,25 +695,6 @@ __global__ __launch_bounds__(256) void fwht_small_kernel(
     }
 }
 
-constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
-
-// Raising a kernel's dynamic LDS limit above the 64 KiB default needs
-// hipFuncSetAttribute once per (kernel, device).
-template <class Kernel>
-int ensure_lds(Kernel kernel, size_t bytes)
-{
-    static std::atomic<int> granted[64];
-    if (bytes <= 65536) return 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (granted[dev].load(std::memory_order_relaxed)) return 0;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-    if (e != hipSuccess) return (int)e;
-    granted[dev].store(1, std::memory_order_relaxed);
-    return 0;
-}
-
 struct GemvPlan {
     int tpw, wk, wt;
     int64_t wgs;
@@ -823,19 +760,6 @@ int launch_gemv_x(GemvArgs a, hipStream_t stream)
     }
 }
 
-inline int device_cus()
-{
-    static std::atomic<int> cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int c = cus[dev].load(std::memory_order_relaxed);
-    if (c == 0) {
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-            c = 256;
-        cus[dev].store(c, std::memory_order_relaxed);
-    }
-    return c;
-}
 
 // Fused rotation: every workgroup transforms the activations once, so use
 // about one workgroup per CU (up to four tiles per wave) and split K over
@@ -1024,21 +948,6 @@ int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64
         hipLaunchKernelGGL(fwht16_kernel<false>, grid, dim3(threads), lds, st, x, signs, M, K, L, bpw,
                            (int)inverse, y, norm);
     return (int)hipGetLastError();
-}
-
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
-
-int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, const uint16_t *scales,
-                int64_t N, float *y, void *, size_t, void *stream)
-{
-    // First version: 16-row slices through the decode kernel.
-    for (int64_t m0 = 0; m0 < M; m0 += 16) {
-        const int mm = (int)((M - m0) < 16 ? (M - m0) : 16);
-        int rc = launch_gemv(static_cast<const uint16_t *>(x) + m0 * K, false, mm, K, codes, scales, N,
-                             y + m0 * N, false, stream);
-        if (rc) return rc;
-    }
-    return 0;
 }
 
 }  // namespace tern

@@ -355,6 +355,102 @@ def test_gemm_prefill_full_size_sampled(tern, oracle_lib, K, N):
     assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound, what=f"prefill K{K} N{N}")
 
 
+def _gemm_sampled(tern, oracle_lib, M, K, N, seed, t, s, x, cols, what):
+    """Run tern_gemm on the full problem; compare sampled output columns."""
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = tern.tern_gemm(x_to_device(x), codes_d, scales_d)
+    torch().cuda.synchronize()
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t[cols]), s[cols], K)
+    assert_matmul_close(y_to_host(y)[:, cols], y_ref, bound, what=what)
+    return y
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (600, 4096, 700),    # ragged row and column tiles; every tile split in pieces
+    (1024, 512, 1024),   # ranges of exactly one tile: no pieces, no workspace
+    (4000, 384, 3900),   # ranges of 5-6 groups: whole tiles mixed with pieces
+    (300, 17408, 96),    # long K split over many workgroups
+])
+def test_gemm_work_split_cases(tern, oracle_lib, M, K, N):
+    seed = 7 * M + 3 * K + N
+    print(f"gemm split case M={M} K={K} N={N} ws={tern.tern_gemm_workspace_bytes(M, N, K)}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    cols = sampled_rows(N, 40, seed)
+    _gemm_sampled(tern, oracle_lib, M, K, N, seed, t, s, x, cols, f"gemm M{M} K{K} N{N}")
+
+
+def test_gemm_zero_scale_groups(tern, oracle_lib):
+    """Zero scales: whole columns, the first and last group of a column, and
+    random groups (the scale-rescaling path must skip them)."""
+    M, K, N, seed = 300, 2048, 160, 77
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    rng = np.random.default_rng(seed)
+    s[rng.random(s.shape) < 0.2] = 0
+    s[3, :] = 0
+    s[5, 0] = 0
+    s[6, -1] = 0
+    s[7, :-1] = 0
+    s[8, 1:] = 0
+    s[9, ::2] = 0x8000  # -0.0
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    cols = np.arange(N)
+    _gemm_sampled(tern, oracle_lib, M, K, N, seed, t, s, x, cols, "gemm zero scales")
+
+
+def test_gemm_wide_scale_range(tern, oracle_lib):
+    """Group scales spread over 2^-24 .. 2^15 (fp16 subnormals to near max),
+    negative ones too: the per-group rescaling keeps the error bound."""
+    M, K, N, seed = 260, 8192, 130, 78
+    t = synth.ternary(seed, N, K, 0.35)
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.uniform(-24, 15, size=(N, K // 128)))
+    sgn = np.where(rng.random((N, K // 128)) < 0.2, -1.0, 1.0)
+    s = (sgn * mag).astype(np.float16).view(np.uint16)
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    cols = np.arange(N)
+    _gemm_sampled(tern, oracle_lib, M, K, N, seed, t, s, x, cols, "gemm wide scales")
+
+
+def test_gemm_integer_exact_and_deterministic(tern, oracle_lib):
+    """Small-integer activations with unit scales: every partial sum is an
+    integer below 2^24, so the result is exact; and repeated calls agree
+    bit for bit."""
+    T = torch()
+    M, K, N, seed = 520, 3072, 300, 79
+    t = synth.ternary(seed, N, K, 0.35)
+    s = np.full((N, K // 128), 0x3C00, dtype=np.uint16)  # 1.0
+    rng = np.random.default_rng(seed)
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    x = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    xd = x_to_device(x)
+    y1 = tern.tern_gemm(xd, codes_d, scales_d)
+    y2 = tern.tern_gemm(xd, codes_d, scales_d)
+    T.cuda.synchronize()
+    exact = xi.astype(np.float64) @ t.astype(np.float64).T
+    assert np.array_equal(y_to_host(y1), exact)
+    assert T.equal(y1, y2)
+
+
+def test_gemm_k_zero_and_empty(tern):
+    T = torch()
+    x = T.zeros((300, 0), dtype=T.bfloat16, device="cuda")
+    codes = T.zeros((70, 0), dtype=T.int32, device="cuda")
+    scales = T.zeros((70, 0), dtype=T.int16, device="cuda")
+    y = T.full((300, 70), 7.0, device="cuda")
+    tern.tern_gemm(x, codes, scales, out=y)
+    T.cuda.synchronize()
+    assert (y == 0).all()
+    y0 = T.full((0, 70), 7.0, device="cuda")
+    tern.tern_gemm(T.zeros((0, 128), dtype=T.bfloat16, device="cuda"),
+                   T.zeros((70, 8), dtype=T.int32, device="cuda"),
+                   T.zeros((70, 1), dtype=T.int16, device="cuda"), out=y0)
+    T.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # HIP graph capture of the decode step: every replay equals eager execution
 # ---------------------------------------------------------------------------
