@@ -58,12 +58,18 @@ namespace {
 
 #include "tern_device.h"
 
-constexpr int kGemmBM = 256, kGemmBN = 128;
+constexpr int kGemmBM = 128, kGemmBN = 512;
+constexpr int kGemmWaves = 8;                              // one per 64 output columns
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
 constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
-constexpr int kGemmStageBytes = kGemmBM * kGemmRowBytes;   // 64 KiB
+constexpr int kGemmStageBytes = kGemmBM * kGemmRowBytes;   // 32 KiB
+constexpr int kGemmDmaPerWave = kGemmStageBytes / (kGemmThreads * 16);  // 4
 constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
 constexpr int kGemmMinUnits = 4;                           // groups per range, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
+// s_waitcnt operand: vmcnt(n), expcnt and lgkmcnt not waited for
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -81,19 +87,34 @@ struct GemmArgs {
     int64_t units;          // tiles * G
 };
 
-// 2-bit fields 0, 2, .., 14 of x to the low half and 1, 3, .., 15 to the
-// high half (field i moves to (i >> 1) + 8 (i & 1)): three swaps of adjacent
-// index bits, each a masked exchange of fields.
-__device__ __forceinline__ unsigned unshuffle2(unsigned x)
+// Weight operands without per-pair shifts.  For a code word w, plane s
+// (s = 0..3) is ((w ^ 0x55555555) << (6 - 2 s)) & m: byte b of it holds the
+// flipped slot 4 b + s at bits 7..6 and zeros elsewhere (m = 0xC0C0C0C0, or
+// 0 for a zero-scale group).  A bfloat16 pair of the MFMA operand -- slots
+// 2p and 2p + 1 at bits 15..14 and 31..30 -- is then one byte permute of
+// two planes: byte p >> 1 of plane 2 (p & 1) into byte 1, the same byte of
+// plane 2 (p & 1) + 1 into byte 3, zeros elsewhere.
+constexpr unsigned kPlaneMask = 0xC0C0C0C0u;
+
+__device__ __forceinline__ void code_planes(unsigned w, unsigned m, unsigned (&t)[4])
 {
-    unsigned t;
-    t = (x ^ (x >> 2)) & 0x0C0C0C0Cu;
-    x ^= t ^ (t << 2);
-    t = (x ^ (x >> 4)) & 0x00F000F0u;
-    x ^= t ^ (t << 4);
-    t = (x ^ (x >> 8)) & 0x0000FF00u;
-    x ^= t ^ (t << 8);
-    return x;
+    t[0] = ((w << 6) ^ (kFlip << 6)) & m;
+    t[1] = ((w << 4) ^ (kFlip << 4)) & m;
+    t[2] = ((w << 2) ^ (kFlip << 2)) & m;
+    t[3] = (w ^ kFlip) & m;
+}
+
+// MFMA B operand for slots 8h .. 8h + 7 of a word (element e = slot 8h + e).
+__device__ __forceinline__ bf16x8_t operand_from_planes(const unsigned (&t)[4], int h)
+{
+    u32x4_t p;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int pair = 4 * h + v, b = pair >> 1;
+        const unsigned sel = 0x0Cu | ((unsigned)b << 8) | (0x0Cu << 16) | ((4u + b) << 24);
+        p[v] = (pair & 1) ? __builtin_amdgcn_perm(t[3], t[2], sel) : __builtin_amdgcn_perm(t[1], t[0], sel);
+    }
+    return __builtin_bit_cast(bf16x8_t, p);
 }
 
 // Range of logical workgroup w: units [w U / P, (w + 1) U / P).
@@ -113,20 +134,20 @@ __device__ __forceinline__ int gemm_logical_wg(int raw, int P)
 
 // Position in the tile of accumulator element e in MFMA register order
 // e = ((((wave * 4 + i) * 2 + j) * 16 + v) * 64 + lane): lane (c, g) of
-// sub-tile (i, j) holds rows 8 (v >> 2) + 4 g + (v & 3), column c.
+// sub-tile (i, j) holds row 32 i + 8 (v >> 2) + 4 g + (v & 3), column
+// 64 wave + 32 j + c.
 __device__ __forceinline__ void gemm_elem_pos(int e, int &mr, int &nc)
 {
     const int lane = e & 63, v = (e >> 6) & 15, j = (e >> 10) & 1, i = (e >> 11) & 3, wave = e >> 13;
-    mr = 128 * (wave & 1) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    nc = 64 * (wave >> 1) + 32 * j + (lane & 31);
+    mr = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    nc = 64 * wave + 32 * j + (lane & 31);
 }
 
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
     const int col = lane & 31, lg = lane >> 5;
     const int G = a.G;
     const int64_t KW = a.K / 16;
@@ -135,17 +156,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
     const int w = __builtin_amdgcn_readfirstlane(gemm_logical_wg(blockIdx.x, a.P));
     const int64_t u0 = gemm_range_start(w, a), u1 = gemm_range_start(w + 1, a);
 
-    // Loads to LDS: wave instruction b fills 1 KiB = rows 64 wave + 4 b ..
-    // + 3 of a stage; lane l writes position l & 15 of row 64 wave + 4 b +
+    // Loads to LDS: wave instruction b fills 1 KiB = rows 16 wave + 4 b ..
+    // + 3 of a stage; lane l writes position l & 15 of row 16 wave + 4 b +
     // (l >> 4), i.e. chunk (l & 15) ^ (row & 15) of that row.
-    unsigned voff[16];
+    unsigned voff[kGemmDmaPerWave];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const unsigned r = 64 * wave + 4 * b + (lane >> 4);
+    for (int b = 0; b < kGemmDmaPerWave; ++b) {
+        const unsigned r = 16 * wave + 4 * b + (lane >> 4);
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
-    // A operand reads: row 128 wm + 32 i + col, chunk 8 lg + kappa
-    const unsigned a_row = (128 * wm + col) * kGemmRowBytes;
+    // A operand reads: row 32 i + col, chunk 8 lg + kappa at position
+    // (8 lg + kappa) ^ (col & 15)
+    const unsigned a_row = col * kGemmRowBytes;
     const unsigned a_sw = (8 * lg) ^ (col & 15);
 
     for (int64_t u = u0; u < u1;) {
@@ -166,7 +188,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
         const uint16_t *srow[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            int64_t n = n0 + 64 * wn + 32 * j + col;
+            int64_t n = n0 + 64 * wave + 32 * j + col;
             n = n < a.N ? n : a.N - 1;
             crow[j] = a.codes + n * KW + 4 * lg;
             srow[j] = a.scales + n * G;
@@ -177,9 +199,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
             __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(xtile + (int64_t)g * kGroup), (short)0, (int)(tile_bytes - 256u * (unsigned)g),
                 (int)kBufferDword3);
-            unsigned char *dst = smem + sb * kGemmStageBytes + wave * 16384;
+            unsigned char *dst = smem + sb * kGemmStageBytes + wave * (kGemmDmaPerWave * 1024);
 #pragma unroll
-            for (int b = 0; b < 16; ++b)
+            for (int b = 0; b < kGemmDmaPerWave; ++b)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 1024 * b), 16, voff[b], 0, 0, 0);
         };
 
@@ -190,112 +212,117 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) T[i][j][v] = 0.0f;
-        float s_c[2] = {0.0f, 0.0f};
-
-        // group ka: codes, scale (s_c, mask) and activations into stage 0
-        u32x4_t cb[2];
-        uint32_t sv[2];
+        float s_c[2];
         unsigned mask[2];
+        u32x4_t cb[2];
+        uint32_t s1[2];
+
+        // prologue: activations of groups ka and ka + 1 (clamped) into
+        // stages 0 and 1, codes and scale of group ka, scale of ka + 1
         stage(ka, 0);
+        stage(ka + 1 < kb ? ka + 1 : ka, 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             cb[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)ka * kWordsPerGroup);
             const float s0 = half_to_float(srow[j][ka]);
             s_c[j] = s0;
-            mask[j] = s0 != 0.0f ? 0xffffffffu : 0u;
+            mask[j] = s0 != 0.0f ? kPlaneMask : 0u;
+            s1[j] = srow[j][ka + 1 < kb ? ka + 1 : ka];
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
+        int sb = 0;
         for (int gg = ka; gg < kb; ++gg) {
-            const int sb = (gg - ka) & 1;
             const unsigned char *cur = smem + sb * kGemmStageBytes;
             const bool more = gg + 1 < kb;
-            const int gn = more ? gg + 1 : gg;  // the last prefetch repeats a group
+            const int g1 = more ? gg + 1 : gg;               // codes: one group ahead
+            const int g2 = gg + 2 < kb ? gg + 2 : kb - 1;    // scales, activations: two ahead
+            const int sb2 = sb == 0 ? 2 : sb - 1;            // (sb + 2) % 3
 
-            // next group's codes, scales and activations, issued before any
-            // of this group's matrix work
+            // issue order matters for the counted wait below: scales of g2,
+            // codes of g1, then the activations of g2
+            uint32_t s2[2];
             u32x4_t cbn[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) sv[j] = srow[j][gn];
+            for (int j = 0; j < 2; ++j) s2[j] = srow[j][g2];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                cbn[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)gn * kWordsPerGroup);
-            stage(gn, sb ^ 1);
+                cbn[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)g1 * kWordsPerGroup);
+            stage(g2, sb2);
             __builtin_amdgcn_sched_barrier(0);
 
-            // this group's weight operands
-            unsigned wf[2][4];
+            // rescale factor to group gg + 1 (its scale arrived a group ago)
+            float r[2];
+            unsigned mask_next[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) wf[j][q] = (unshuffle2(cb[j][q]) ^ kFlip) & mask[j];
+            for (int j = 0; j < 2; ++j) {
+                const float s_new = half_to_float((uint16_t)s1[j]);
+                const bool nz = __builtin_unpredictable(more && s_new != 0.0f);  // selects, no branch
+                const float ratio = s_c[j] * __builtin_amdgcn_rcpf(s_new);
+                r[j] = nz ? ratio : 1.0f;
+                mask_next[j] = __builtin_unpredictable(!more || s_new != 0.0f) ? kPlaneMask : 0u;
+                s_c[j] = nz ? s_new : s_c[j];
+            }
 
             const unsigned char *ap = cur + a_row;
-            bf16x8_t aop[4], anx[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes + 16 * a_sw);
+            for (int q = 0; q < 4; ++q) {
+                unsigned t[2][4];
 #pragma unroll
-            for (int kappa = 0; kappa < 8; ++kappa) {
-                if (kappa < 7) {
+                for (int j = 0; j < 2; ++j) code_planes(cb[j][q], mask[j], t[j]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kappa = 2 * q + h;
+                    bf16x8_t aop[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        anx[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
-                                                                     16 * (a_sw ^ (kappa + 1)));
-                }
-                bf16x8_t bop[2];
+                        aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
+                                                                     16 * (a_sw ^ kappa));
+                    bf16x8_t bop[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bop[j] = weights_operand(wf[j][kappa >> 1], kappa & 1);
-                if (kappa == 7) {
-                    // rescale to the next group's scale right after each
-                    // tile's last product of this group (kept here: the
-                    // scale loads must not be waited for any earlier)
-                    __builtin_amdgcn_sched_barrier(0);
-                    float r[2];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float s_new = half_to_float((uint16_t)sv[j]);
-                        const bool nz = more && s_new != 0.0f;
-                        r[j] = nz ? s_c[j] * __builtin_amdgcn_rcpf(s_new) : 1.0f;
-                        s_c[j] = nz ? s_new : s_c[j];
-                        mask[j] = (!more || s_new != 0.0f) ? 0xffffffffu : 0u;
-                    }
+                    for (int j = 0; j < 2; ++j) bop[j] = operand_from_planes(t[j], h);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
                             T[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[j], T[i][j], 0, 0, 0);
-                            T[i][j] *= r[j];
+                            // Horner step after each tile's last product of the group
+                            if (kappa == 7) T[i][j] *= r[j];
                         }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            T[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[j], T[i][j], 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) aop[i] = anx[i];
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) cb[j] = cbn[j];
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            for (int j = 0; j < 2; ++j) {
+                cb[j] = cbn[j];
+                s1[j] = s2[j];
+                mask[j] = mask_next[j];
+            }
+            // everything but this group's activation prefetch has landed,
+            // in particular the stage of group gg + 1; a plain barrier (no
+            // memory fence, which would wait for the prefetch too) then
+            // publishes it to all waves.  Every LDS read of this group was
+            // consumed by an MFMA above, so the stage refilled next is free.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave));
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            sb = sb == 2 ? 0 : sb + 1;
         }
 
         // epilogue: lane (col, lg) of sub-tile (i, j) holds rows
-        // 8 (v >> 2) + 4 lg + (v & 3) of the sub-tile, column col
+        // 32 i + 8 (v >> 2) + 4 lg + (v & 3), column 64 wave + 32 j + col
         if (ka == 0 && kb == G) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int64_t n = n0 + 64 * wn + 32 * j + col;
+                const int64_t n = n0 + 64 * wave + 32 * j + col;
                 const float f = -0.5f * s_c[j];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int64_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * lg + (v & 3);
+                        const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * lg + (v & 3);
                         if (m < a.M && n < a.N) a.y[m * a.N + n] = T[i][j][v] * f;
                     }
             }
@@ -310,11 +337,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a)
                     for (int v = 0; v < 16; ++v) out[((i * 2 + j) * 16 + v) * 64] = T[i][j][v] * f;
             }
         }
+        // the next segment's prologue overwrites stages 0 and 1; the last
+        // prefetch of this segment may still be landing in one of them
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 }
 
 // Tiles split between workgroups: y = sum of the pieces in K order.
-// grid (tiles, 16) x 256 threads, 8 outputs per thread.
+// grid (tiles, kGemmTileElems / 2048) x 256 threads, 8 outputs per thread.
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmArgs a)
 {
     const int64_t tile = blockIdx.x;
@@ -347,7 +378,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *y, int64_t count)
 }
 
 // P ranges of at least kGemmMinUnits groups, at most one per CU (the
-// kernel's LDS, two 64 KiB stages, allows one workgroup per CU).
+// kernel's LDS, three 32 KiB stages, allows one workgroup per CU).
 GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
 {
     GemmArgs a{};
@@ -381,7 +412,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return gemm_splits_tiles(a) ? (size_t)a.P * 2 * kGemmTileElems * sizeof(float) : 0;
 }
 
-int64_t gemm_max_k() { return ((int64_t)1 << 31) / (2 * kGemmBM) - kGroup; }
+int64_t gemm_max_k() { return ((int64_t)1 << 22) - kGroup; }
 
 int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, const uint16_t *scales,
                 int64_t N, float *y, void *workspace, size_t, void *stream)
@@ -400,14 +431,14 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
     a.scales = scales;
     a.y = y;
     a.partial = static_cast<float *>(workspace);
-    const size_t lds = 2 * (size_t)kGemmStageBytes;
+    const size_t lds = kGemmStages * (size_t)kGemmStageBytes;
     int rc = ensure_lds(gemm_kernel, lds);
     if (rc) return rc;
-    hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)a.P), dim3(256), lds, st, a);
+    hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
     rc = (int)hipGetLastError();
     if (rc || !gemm_splits_tiles(a)) return rc;
     const int64_t tiles = a.units / a.G;
-    hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)tiles, kGemmTileElems / (8 * 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)tiles, kGemmTileElems / 2048), dim3(256), 0, st,
                        a);
     return (int)hipGetLastError();
 }
