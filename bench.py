@@ -39,8 +39,9 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="rotated",
-                   choices=["rotated", "sweep", "prefill", "all"],
-                   help="rotated: the headline step; sweep / prefill: extra measurements")
+                   choices=["rotated", "sweep", "prefill", "copy", "all"],
+                   help="rotated: the headline step; sweep / prefill: extra measurements; "
+                        "copy: a plain device copy of known size (counter calibration)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline line only")
     return p.parse_args()
@@ -48,6 +49,47 @@ def parse():
 
 def gemv_bytes(M, K, N, x_bytes):
     return N * K // 4 + 2 * N * K // 128 + M * K * x_bytes + M * N * 4
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_rotated_M1_K4096_N12288_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "ternary_weight_g128_amd", "csrc", f)
+                  for f in ("tern_kernels.hip", "tern_device.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    src = h.hexdigest()
+    if fields.get("kernel_source_sha256") != src:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_copy(torch, nbytes=256 << 20, reps=5):
+    """A plain device-to-device copy of nbytes (reads nbytes, writes nbytes):
+    the reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    src = torch.randn(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}
 
 
 def rotated_step_bytes(w):
@@ -159,7 +201,7 @@ def bench_rotated(args, tern, torch, synth):
         "value": value,
         "ms_per_step": ms_per_step,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "detail": {"kernel": "gemv_kernel<2, true, TPW, true, 1> (fused rotation + GEMV)",
                    "kernel_us": kernel_us, "step_bytes": step_bytes,
                    "two_launch_step_us": 1e3 * two_ms / args.steps,
@@ -261,6 +303,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.workload == "copy":
+        print(json.dumps({"copy": bench_copy(torch)}))
+        return
     if args.workload in ("sweep", "prefill"):
         fn = bench_sweep if args.workload == "sweep" else bench_prefill
         print(json.dumps({args.workload: fn(tern, torch, synth, args.steps)}))
