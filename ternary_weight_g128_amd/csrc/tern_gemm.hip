@@ -5,13 +5,13 @@
 // "CUDA (NVIDIA GPUs)": codes unpacked and scaled inside the kernel, never a
 // dense FP16 weight tensor).  bfloat16 activations, binary32 result.
 //
-// Tiles.  A workgroup of four waves (2 x 2) computes a 256 (m) x 128 (n)
-// output tile; a wave owns 128 x 64 as 4 x 2 sub-tiles of
-// v_mfma_f32_32x32x16_bf16.  One 128-K scale group is one pipeline stage:
-// the group's 256 x 128 activations (64 KiB) go straight from memory into
-// LDS with buffer loads to LDS (no register staging), double buffered, while
-// the matrix cores work on the previous group.  Rows past M read as zero
-// through the buffer's range check.
+// Tiles.  A workgroup of eight waves computes a 64 (m) x 512 (n) output
+// tile; wave w owns columns 64w .. 64w + 63 as 2 x 2 sub-tiles of
+// v_mfma_f32_32x32x16_bf16 (accumulators in VGPRs, two waves per SIMD).  One
+// 128-K scale group is one pipeline stage: the group's 64 x 128 activations
+// (16 KiB) go straight from memory into LDS with buffer loads to LDS (no
+// register staging), three stages deep, two groups ahead of the matrix
+// cores.  Rows past M read as zero through the buffer's range check.
 //
 // Operands.  For sub-tile column j, lane l holds output column l & 31 and
 // lane group g = l >> 5 loads code words 4g..4g+3 of that column's group.
@@ -33,16 +33,13 @@
 // was accumulated before it.  A group with a zero scale contributes nothing:
 // its code words are masked to zero and s_c is kept.
 //
-// Work split (balanced K ranges).  The (tile, group) pairs are numbered
-// unit = tile * G + group and cut into P equal contiguous ranges, one per
-// workgroup and at most one workgroup per CU, so no CU idles through a
-// short last round.  A workgroup walks its range tile by tile: a tile it
-// covers from the first to the last group goes straight to y; a piece of a
-// tile goes to a partial-sum slot (slot 0 for the first piece of the range,
-// slot 1 for the last) and a second kernel adds each tile's pieces in K
-// order, so the result does not depend on timing.  Consecutive tiles share a
-// column block (the same codes), and consecutive ranges run on one XCD, so
-// that XCD's L2 serves the codes to both row tiles.
+// Work split.  P workgroups (at most one per CU) take whole tiles round
+// robin for R = tiles / P rounds.  The r leftover tiles are cut along K into
+// s equal pieces (s chosen on the host to balance the last round against the
+// partial-sum traffic); piece j of the r * s goes to workgroup j mod P and
+// into partial slot j, and a second kernel adds each leftover tile's s pieces
+// in K order, so the result does not depend on timing.  Consecutive tiles
+// share a column block (the same codes).
 
 #include <hip/hip_runtime.h>
 
@@ -58,15 +55,16 @@ namespace {
 
 #include "tern_device.h"
 
-constexpr int kGemmBM = 128, kGemmBN = 512;
+constexpr int kGemmMI = 2;                                 // 32-row sub-tiles per wave
+constexpr int kGemmBM = 32 * kGemmMI, kGemmBN = 512;
 constexpr int kGemmWaves = 8;                              // one per 64 output columns
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
 constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
-constexpr int kGemmStageBytes = kGemmBM * kGemmRowBytes;   // 32 KiB
-constexpr int kGemmDmaPerWave = kGemmStageBytes / (kGemmThreads * 16);  // 4
+constexpr int kGemmStageBytes = kGemmBM * kGemmRowBytes;   // 16 KiB
+constexpr int kGemmDmaPerWave = kGemmStageBytes / (kGemmThreads * 16);  // 2
 constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
-constexpr int kGemmMinUnits = 4;                           // groups per range, at least
+constexpr int kGemmMinPiece = 4;                           // groups per K piece, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
 // s_waitcnt operand: vmcnt(n), expcnt and lgkmcnt not waited for
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -79,12 +77,15 @@ struct GemmArgs {
     const uint32_t *codes;  // [N][K/16]
     const uint16_t *scales; // [N][K/128]
     float *y;               // [M][N]
-    float *partial;         // [P][2][kGemmTileElems], MFMA register order
+    float *partial;         // [r * s][kGemmTileElems], MFMA register order
     int64_t M, N;
     int K, G;               // G = K / 128
     int tiles_m;
-    int P;                  // workgroups (ranges)
-    int64_t units;          // tiles * G
+    int P;                  // workgroups
+    int64_t tiles;          // tiles_m * tiles_n
+    int64_t full;           // R * P: tiles done whole, round robin
+    int split;              // s: K pieces of each leftover tile (1: none left)
+    int64_t items;          // r * s leftover pieces
 };
 
 // Weight operands without per-pair shifts.  For a code word w, plane s
@@ -117,28 +118,14 @@ __device__ __forceinline__ bf16x8_t operand_from_planes(const unsigned (&t)[4], 
     return __builtin_bit_cast(bf16x8_t, p);
 }
 
-// Range of logical workgroup w: units [w U / P, (w + 1) U / P).
-__device__ __forceinline__ int64_t gemm_range_start(int64_t w, const GemmArgs &a)
-{
-    return w * a.units / a.P;
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs; number them so that
-// each XCD gets a contiguous block of ranges.
-__device__ __forceinline__ int gemm_logical_wg(int raw, int P)
-{
-    const int q = P >> 3, r = P & 7;
-    const int xcd = raw & 7, k = raw >> 3;
-    return xcd * q + (xcd < r ? xcd : r) + k;
-}
-
 // Position in the tile of accumulator element e in MFMA register order
-// e = ((((wave * 4 + i) * 2 + j) * 16 + v) * 64 + lane): lane (c, g) of
+// e = ((((wave * MI + i) * 2 + j) * 16 + v) * 64 + lane): lane (c, g) of
 // sub-tile (i, j) holds row 32 i + 8 (v >> 2) + 4 g + (v & 3), column
 // 64 wave + 32 j + c.
 __device__ __forceinline__ void gemm_elem_pos(int e, int &mr, int &nc)
 {
-    const int lane = e & 63, v = (e >> 6) & 15, j = (e >> 10) & 1, i = (e >> 11) & 3, wave = e >> 13;
+    const int lane = e & 63, v = (e >> 6) & 15, j = (e >> 10) & 1;
+    const int i = (e >> 11) % kGemmMI, wave = (e >> 11) / kGemmMI;
     mr = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     nc = 64 * wave + 32 * j + (lane & 31);
 }
@@ -153,16 +140,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
     const int64_t KW = a.K / 16;
     const unsigned row_bytes = 2u * (unsigned)a.K;
 
-    const int w = __builtin_amdgcn_readfirstlane(gemm_logical_wg(blockIdx.x, a.P));
-    const int64_t u0 = gemm_range_start(w, a), u1 = gemm_range_start(w + 1, a);
+    const int w = blockIdx.x;
+    // work items: whole tiles w, w + P, .. below a.full, then leftover
+    // pieces j = w, w + P, .. below a.items
+    const int64_t n_full = w < a.full % a.P ? a.full / a.P + 1 : a.full / a.P;
+    const int64_t n_part = a.items > w ? (a.items - 1 - w) / a.P + 1 : 0;
 
-    // Loads to LDS: wave instruction b fills 1 KiB = rows 16 wave + 4 b ..
-    // + 3 of a stage; lane l writes position l & 15 of row 16 wave + 4 b +
-    // (l >> 4), i.e. chunk (l & 15) ^ (row & 15) of that row.
+    // Loads to LDS: wave instruction b fills 1 KiB = rows 4 (DW wave + b) ..
+    // + 3 of a stage; lane l writes position l & 15 of its row, i.e. chunk
+    // (l & 15) ^ (row & 15) of that row.
     unsigned voff[kGemmDmaPerWave];
 #pragma unroll
     for (int b = 0; b < kGemmDmaPerWave; ++b) {
-        const unsigned r = 16 * wave + 4 * b + (lane >> 4);
+        const unsigned r = 4 * (kGemmDmaPerWave * wave + b) + (lane >> 4);
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
     // A operand reads: row 32 i + col, chunk 8 lg + kappa at position
@@ -170,12 +160,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
     const unsigned a_row = col * kGemmRowBytes;
     const unsigned a_sw = (8 * lg) ^ (col & 15);
 
-    for (int64_t u = u0; u < u1;) {
-        const int64_t tile = u / G;
-        const int ka = (int)(u - tile * G);
-        const int kb = (int)(u1 - tile * G < G ? u1 - tile * G : G);
-        const int slot = u == u0 ? 0 : 1;
-        u = tile * G + kb;
+    for (int64_t it = 0; it < n_full + n_part; ++it) {
+        const bool whole = it < n_full;
+        const int64_t pj = (it - n_full) * a.P + w;           // leftover piece
+        const int64_t tile = whole ? w + it * a.P : a.full + pj / a.split;
+        const int piece = whole ? 0 : (int)(pj % a.split);
+        const int ka = whole ? 0 : (int)((int64_t)piece * G / a.split);
+        const int kb = whole ? G : (int)((int64_t)(piece + 1) * G / a.split);
 
         const int64_t tm = tile % a.tiles_m, tn = tile / a.tiles_m;
         const int64_t m0 = tm * kGemmBM, n0 = tn * kGemmBN;
@@ -205,13 +196,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 1024 * b), 16, voff[b], 0, 0, 0);
         };
 
-        f32x16_t T[4][2];
+        f32x16_t T[kGemmMI][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kGemmMI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) T[i][j][v] = 0.0f;
+                for (int v = 0; v < 16; ++v) T[i][jj][v] = 0.0f;
         float s_c[2];
         unsigned mask[2];
         u32x4_t cb[2];
@@ -274,16 +265,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kappa = 2 * q + h;
-                    bf16x8_t aop[4];
+                    bf16x8_t aop[kGemmMI];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < kGemmMI; ++i)
                         aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
                                                                      16 * (a_sw ^ kappa));
                     bf16x8_t bop[2];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) bop[j] = operand_from_planes(t[j], h);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < kGemmMI; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
                             T[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[j], T[i][j], 0, 0, 0);
@@ -313,13 +304,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
 
         // epilogue: lane (col, lg) of sub-tile (i, j) holds rows
         // 32 i + 8 (v >> 2) + 4 lg + (v & 3), column 64 wave + 32 j + col
-        if (ka == 0 && kb == G) {
+        if (whole) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int64_t n = n0 + 64 * wave + 32 * j + col;
                 const float f = -0.5f * s_c[j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < kGemmMI; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * lg + (v & 3);
@@ -327,47 +318,50 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
                     }
             }
         } else {
-            float *out = a.partial + ((int64_t)w * 2 + slot) * kGemmTileElems + wave * 8192 + lane;
+            float *out = a.partial + pj * kGemmTileElems + wave * (kGemmMI * 2048) + lane;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float f = -0.5f * s_c[j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < kGemmMI; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) out[((i * 2 + j) * 16 + v) * 64] = T[i][j][v] * f;
             }
         }
-        // the next segment's prologue overwrites stages 0 and 1; the last
-        // prefetch of this segment may still be landing in one of them
+        // the next item's prologue overwrites stages 0 and 1; the last
+        // prefetch of this item may still be landing in one of them
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 }
 
-// Tiles split between workgroups: y = sum of the pieces in K order.
-// grid (tiles, kGemmTileElems / 2048) x 256 threads, 8 outputs per thread.
+// Leftover tiles: y = sum of their a.split K pieces, in K order.
+// grid (leftover tiles, kGemmTileElems / 256) x 256 threads, one output per
+// thread; the piece loads are issued together (up to 8 at a time) and added
+// in K order.
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmArgs a)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t first = tile * a.G, last = first + a.G - 1;
-    // logical workgroup holding unit u: the largest w with w U / P <= u
-    const int64_t wa = ((first + 1) * a.P - 1) / a.units;
-    const int64_t wb = ((last + 1) * a.P - 1) / a.units;
-    if (wa == wb) return;  // written directly
+    const int64_t lt = blockIdx.x;                 // leftover tile
+    const int64_t tile = a.full + lt;
     const int64_t m0 = (tile % a.tiles_m) * kGemmBM, n0 = (tile / a.tiles_m) * kGemmBN;
+    const int e = blockIdx.y * 256 + threadIdx.x;
+    const float *src = a.partial + lt * a.split * kGemmTileElems + e;
+    float s = 0.0f;
+    for (int p0 = 0; p0 < a.split; p0 += 8) {
+        float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int e = (blockIdx.y * 8 + k) * 256 + threadIdx.x;
-        float s = 0.0f;
-        for (int64_t w = wa; w <= wb; ++w) {
-            const int slot = w * a.units / a.P >= first ? 0 : 1;
-            s += a.partial[(w * 2 + slot) * kGemmTileElems + e];
+        for (int q = 0; q < 8; ++q) {
+            const int p = p0 + q < a.split ? p0 + q : a.split - 1;
+            v[q] = src[(int64_t)p * kGemmTileElems];
         }
-        int mr, nc;
-        gemm_elem_pos(e, mr, nc);
-        const int64_t m = m0 + mr, n = n0 + nc;
-        if (m < a.M && n < a.N) a.y[m * a.N + n] = s;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (p0 + q < a.split) s += v[q];
     }
+    int mr, nc;
+    gemm_elem_pos(e, mr, nc);
+    const int64_t m = m0 + mr, n = n0 + nc;
+    if (m < a.M && n < a.N) a.y[m * a.N + n] = s;
 }
 
 // K = 0: y = 0 (an empty sum).
@@ -377,8 +371,13 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *y, int64_t count)
         y[i] = 0.0f;
 }
 
-// P ranges of at least kGemmMinUnits groups, at most one per CU (the
-// kernel's LDS, three 32 KiB stages, allows one workgroup per CU).
+// Work split over C = #CUs (one workgroup per CU: the LDS stages and 512
+// threads allow one): R = tiles / C rounds of whole tiles, then the
+// r = tiles mod C leftover tiles in s K pieces each.  s minimises the
+// modelled time in units of one tile-group on one CU (~1.5 us): the busiest
+// workgroup's groups plus the round trip of all partial sums through HBM
+// (the whole GPU moves about 6 MiB in that time).  P workgroups run: C, or
+// fewer when there are fewer work items.
 GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
 {
     GemmArgs a{};
@@ -387,19 +386,37 @@ GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
     a.K = (int)K;
     a.G = (int)(K / kGroup);
     a.tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
-    const int64_t tiles = a.tiles_m * ((N + kGemmBN - 1) / kGemmBN);
-    a.units = tiles * a.G;
-    int64_t P = a.units / kGemmMinUnits;
-    const int cus = device_cus();
-    P = P < cus ? P : cus;
-    a.P = (int)(P < 1 ? 1 : P);
+    a.tiles = a.tiles_m * ((N + kGemmBN - 1) / kGemmBN);
+    const int64_t C = device_cus();
+    const int64_t R = a.tiles / C, r = a.tiles - R * C;
+    a.split = 1;
+    if (r > 0) {
+        const double piece_cost = 2.0 * kGemmTileElems * 4 / (6.0 * 1024 * 1024);  // in group times
+        double best = 0.0;
+        const int smax = a.G / kGemmMinPiece > 1 ? a.G / kGemmMinPiece : 1;
+        for (int sp = 1; sp <= smax; ++sp) {
+            const int64_t per_wg = (r * sp + C - 1) / C;                // pieces on the busiest workgroup
+            const int64_t longest = (a.G + sp - 1) / sp;
+            const double t = (double)(R * a.G + per_wg * longest) + (sp > 1 ? piece_cost * (double)(r * sp) : 0.0);
+            if (sp == 1 || t < best) {
+                best = t;
+                a.split = sp;
+            }
+        }
+    }
+    if (a.split == 1) {  // every tile done whole
+        a.full = a.tiles;
+        a.items = 0;
+        a.P = (int)(a.tiles < C ? a.tiles : C);
+    } else {
+        a.full = R * C;
+        a.items = r * a.split;
+        a.P = (int)(R > 0 || a.items >= C ? C : a.items);
+    }
     return a;
 }
 
-bool gemm_splits_tiles(const GemmArgs &a)
-{
-    return a.units > 0 && !(a.units % a.P == 0 && (a.units / a.P) % a.G == 0);
-}
+bool gemm_splits_tiles(const GemmArgs &a) { return a.items > 0; }
 
 }  // namespace
 
@@ -409,7 +426,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     const GemmArgs a = plan_gemm(M, N, K);
-    return gemm_splits_tiles(a) ? (size_t)a.P * 2 * kGemmTileElems * sizeof(float) : 0;
+    return gemm_splits_tiles(a) ? (size_t)a.items * kGemmTileElems * sizeof(float) : 0;
 }
 
 int64_t gemm_max_k() { return ((int64_t)1 << 22) - kGroup; }
@@ -437,9 +454,8 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
     hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
     rc = (int)hipGetLastError();
     if (rc || !gemm_splits_tiles(a)) return rc;
-    const int64_t tiles = a.units / a.G;
-    hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)tiles, kGemmTileElems / 2048), dim3(256), 0, st,
-                       a);
+    hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)(a.items / a.split), kGemmTileElems / 256), dim3(256),
+                       0, st, a);
     return (int)hipGetLastError();
 }
 
