@@ -61,8 +61,11 @@ constexpr int kGemmWaves = 8;                              // one per 64 output 
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
 constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
-constexpr int kGemmStageBytes = kGemmBM * kGemmRowBytes;   // 16 KiB
-constexpr int kGemmDmaPerWave = kGemmStageBytes / (kGemmThreads * 16);  // 2
+constexpr int kGemmXBytes = kGemmBM * kGemmRowBytes;       // 16 KiB of activations
+constexpr int kGemmCBytes = kGemmBN * kWordsPerGroup * 4;  // 16 KiB of code words
+constexpr int kGemmStageBytes = kGemmXBytes + kGemmCBytes;
+constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);   // 2 (activations)
+constexpr int kGemmCDmaPerWave = kGemmCBytes / (kGemmThreads * 16);  // 2 (codes)
 constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
 constexpr int kGemmMinPiece = 4;                           // groups per K piece, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
@@ -155,6 +158,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
         const unsigned r = 4 * (kGemmDmaPerWave * wave + b) + (lane >> 4);
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
+    // Code words to LDS: wave instruction b fills 1 KiB = columns
+    // 64 wave + 32 b .. + 31 of the tile (32 bytes each: the group's 8
+    // words); lane l writes position l & 1 of column (l >> 1), which holds
+    // half (l & 1) ^ ((column >> 3) & 1) of the column's words, so that 16
+    // lanes reading the same half of 16 columns hit distinct banks.
+    unsigned coff[kGemmCDmaPerWave];
+#pragma unroll
+    for (int b = 0; b < kGemmCDmaPerWave; ++b) {
+        const unsigned c = 64 * wave + 32 * b + (lane >> 1);
+        coff[b] = c * (unsigned)(a.K / 4) + 16u * ((lane & 1) ^ ((c >> 3) & 1));
+    }
     // A operand reads: row 32 i + col, chunk 8 lg + kappa at position
     // (8 lg + kappa) ^ (col & 15)
     const unsigned a_row = col * kGemmRowBytes;
@@ -174,18 +188,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
         const uint16_t *xtile = a.x + m0 * a.K;
         const unsigned tile_bytes = (unsigned)rows * row_bytes;
 
-        // this lane's code and scale rows (two sub-tile columns), clamped
-        const uint32_t *crow[2];
+        // this lane's scale rows (two sub-tile columns), clamped
         const uint16_t *srow[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             int64_t n = n0 + 64 * wave + 32 * j + col;
             n = n < a.N ? n : a.N - 1;
-            crow[j] = a.codes + n * KW + 4 * lg;
             srow[j] = a.scales + n * G;
         }
+        const int64_t cols = a.N - n0 < kGemmBN ? a.N - n0 : kGemmBN;
+        const uint32_t *ctile = a.codes + n0 * KW;
+        const unsigned ctile_bytes = (unsigned)cols * (unsigned)(a.K / 4);
 
-        // group g of the tile's rows into stage buffer sb
+        // group g of the tile's activations and code words into stage sb
+        // (columns past N read as zero words; their outputs are dropped)
         auto stage = [&](int g, int sb) {
             __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(xtile + (int64_t)g * kGroup), (short)0, (int)(tile_bytes - 256u * (unsigned)g),
@@ -194,7 +210,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
 #pragma unroll
             for (int b = 0; b < kGemmDmaPerWave; ++b)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 1024 * b), 16, voff[b], 0, 0, 0);
+            __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(ctile + (int64_t)g * kWordsPerGroup), (short)0, (int)(ctile_bytes - 32u * (unsigned)g),
+                (int)kBufferDword3);
+            unsigned char *cdst = smem + sb * kGemmStageBytes + kGemmXBytes + wave * (kGemmCDmaPerWave * 1024);
+#pragma unroll
+            for (int b = 0; b < kGemmCDmaPerWave; ++b)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t *)(cdst + 1024 * b), 16, coff[b], 0, 0, 0);
         };
+        // this lane's four code words of sub-tile column j in stage sb
+        const unsigned c_lds = kGemmXBytes + (64 * wave + col) * 32 + 16 * (lg ^ ((col >> 3) & 1));
 
         f32x16_t T[kGemmMI][2];
 #pragma unroll
@@ -205,20 +230,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
                 for (int v = 0; v < 16; ++v) T[i][jj][v] = 0.0f;
         float s_c[2];
         unsigned mask[2];
-        u32x4_t cb[2];
-        uint32_t s1[2];
+        uint32_t s1[2];           // scale bits of group gg + 1
+        auto gcl = [&](int g) { return g < kb ? g : kb - 1; };
 
-        // prologue: activations of groups ka and ka + 1 (clamped) into
-        // stages 0 and 1, codes and scale of group ka, scale of ka + 1
+        // prologue: activations and codes of groups ka and ka + 1 (clamped)
+        // into stages 0 and 1; scales of groups ka and ka + 1
         stage(ka, 0);
-        stage(ka + 1 < kb ? ka + 1 : ka, 1);
+        stage(gcl(ka + 1), 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            cb[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)ka * kWordsPerGroup);
             const float s0 = half_to_float(srow[j][ka]);
             s_c[j] = s0;
             mask[j] = s0 != 0.0f ? kPlaneMask : 0u;
-            s1[j] = srow[j][ka + 1 < kb ? ka + 1 : ka];
+            s1[j] = srow[j][gcl(ka + 1)];
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -227,20 +251,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
         for (int gg = ka; gg < kb; ++gg) {
             const unsigned char *cur = smem + sb * kGemmStageBytes;
             const bool more = gg + 1 < kb;
-            const int g1 = more ? gg + 1 : gg;               // codes: one group ahead
-            const int g2 = gg + 2 < kb ? gg + 2 : kb - 1;    // scales, activations: two ahead
+            const int g2 = gcl(gg + 2);
             const int sb2 = sb == 0 ? 2 : sb - 1;            // (sb + 2) % 3
 
-            // issue order matters for the counted wait below: scales of g2,
-            // codes of g1, then the activations of g2
+            // scales of group gg + 2 go out first (tiny loads); the stage
+            // of gg + 2 (activations and codes) is issued mid-group below,
+            // so that the waves' loads do not all queue at the CU's address
+            // unit at once
             uint32_t s2[2];
-            u32x4_t cbn[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) s2[j] = srow[j][g2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                cbn[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)g1 * kWordsPerGroup);
-            stage(g2, sb2);
             __builtin_amdgcn_sched_barrier(0);
 
             // rescale factor to group gg + 1 (its scale arrived a group ago)
@@ -256,12 +276,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
                 s_c[j] = nz ? s_new : s_c[j];
             }
 
+            u32x4_t cw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) cw[j] = *reinterpret_cast<const u32x4_t *>(cur + c_lds + 32 * 32 * j);
             const unsigned char *ap = cur + a_row;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (q == 2) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage(g2, sb2);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 unsigned t[2][4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) code_planes(cb[j][q], mask[j], t[j]);
+                for (int j = 0; j < 2; ++j) code_planes(cw[j][q], mask[j], t[j]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kappa = 2 * q + h;
@@ -285,17 +313,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                cb[j] = cbn[j];
                 s1[j] = s2[j];
                 mask[j] = mask_next[j];
             }
-            // everything but this group's activation prefetch has landed,
-            // in particular the stage of group gg + 1; a plain barrier (no
-            // memory fence, which would wait for the prefetch too) then
-            // publishes it to all waves.  Every LDS read of this group was
-            // consumed by an MFMA above, so the stage refilled next is free.
+            // Everything but this group's stage loads has landed, in
+            // particular the stage of group gg + 1; a plain barrier (no
+            // memory fence, which would wait for those loads too) publishes
+            // it to all waves.  Every LDS read of this group was consumed
+            // above, so the stage refilled next group is free.
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave + kGemmCDmaPerWave));
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
