@@ -5,11 +5,14 @@
 // "CUDA (NVIDIA GPUs)": codes unpacked and scaled inside the kernel, never a
 // dense FP16 weight tensor).  bfloat16 activations, binary32 result.
 //
-// Tiles.  A workgroup of eight waves computes a 64 (m) x 512 (n) output
+// Tiles.  A workgroup of four waves computes a 64 (m) x 256 (n) output
 // tile; wave w owns columns 64w .. 64w + 63 as 2 x 2 sub-tiles of
-// v_mfma_f32_32x32x16_bf16 (accumulators in VGPRs, two waves per SIMD).  One
-// 128-K scale group is one pipeline stage: the group's 64 x 128 activations
-// (16 KiB) go straight from memory into LDS with buffer loads to LDS (no
+// v_mfma_f32_32x32x16_bf16 (accumulators in VGPRs).  Two workgroups share
+// each CU, so every SIMD runs one wave of each; their barriers are
+// independent, and one workgroup's barrier waits and VALU phases overlap the
+// other's matrix work.  One 128-K scale group is one pipeline stage: the
+// group's 64 x 128 activations (16 KiB) and the tile's 256 x 8 code words
+// (8 KiB) go straight from memory into LDS with buffer loads to LDS (no
 // register staging), three stages deep, two groups ahead of the matrix
 // cores.  Rows past M read as zero through the buffer's range check.
 //
@@ -33,7 +36,7 @@
 // was accumulated before it.  A group with a zero scale contributes nothing:
 // its code words are masked to zero and s_c is kept.
 //
-// Work split.  P workgroups (at most one per CU) take whole tiles round
+// Work split.  P workgroups (at most two per CU) take whole tiles round
 // robin for R = tiles / P rounds.  The r leftover tiles are cut along K into
 // s equal pieces (s chosen on the host to balance the last round against the
 // partial-sum traffic); piece j of the r * s goes to workgroup j mod P and
@@ -56,16 +59,18 @@ namespace {
 #include "tern_device.h"
 
 constexpr int kGemmMI = 2;                                 // 32-row sub-tiles per wave
-constexpr int kGemmBM = 32 * kGemmMI, kGemmBN = 512;
-constexpr int kGemmWaves = 8;                              // one per 64 output columns
+constexpr int kGemmWaves = 4;                              // one per 64 output columns
+constexpr int kGemmBM = 32 * kGemmMI, kGemmBN = 64 * kGemmWaves;
+constexpr int kGemmWgPerCu = 2;                            // independent workgroups per CU
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
 constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
 constexpr int kGemmXBytes = kGemmBM * kGemmRowBytes;       // 16 KiB of activations
-constexpr int kGemmCBytes = kGemmBN * kWordsPerGroup * 4;  // 16 KiB of code words
+constexpr int kGemmCBytes = kGemmBN * kWordsPerGroup * 4;  // 8 KiB of code words
 constexpr int kGemmStageBytes = kGemmXBytes + kGemmCBytes;
-constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);   // 2 (activations)
+constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);   // 4 (activations)
 constexpr int kGemmCDmaPerWave = kGemmCBytes / (kGemmThreads * 16);  // 2 (codes)
+static_assert(kGemmStages * kGemmStageBytes * kGemmWgPerCu <= 160 * 1024, "LDS for two workgroups per CU");
 constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
 constexpr int kGemmMinPiece = 4;                           // groups per K piece, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
@@ -133,7 +138,7 @@ __device__ __forceinline__ void gemm_elem_pos(int e, int &mr, int &nc)
     nc = 64 * wave + 32 * j + (lane & 31);
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs a)
+__global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const GemmArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
@@ -398,8 +403,8 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *y, int64_t count)
         y[i] = 0.0f;
 }
 
-// Work split over C = #CUs (one workgroup per CU: the LDS stages and 512
-// threads allow one): R = tiles / C rounds of whole tiles, then the
+// Work split over C = 2 x #CUs workgroups (two per CU, which the LDS stages
+// allow): R = tiles / C rounds of whole tiles, then the
 // r = tiles mod C leftover tiles in s K pieces each.  s minimises the
 // modelled time in units of one tile-group on one CU (~1.5 us): the busiest
 // workgroup's groups plus the round trip of all partial sums through HBM
@@ -414,7 +419,7 @@ GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
     a.G = (int)(K / kGroup);
     a.tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
     a.tiles = a.tiles_m * ((N + kGemmBN - 1) / kGemmBN);
-    const int64_t C = device_cus();
+    const int64_t C = kGemmWgPerCu * (int64_t)device_cus();
     const int64_t R = a.tiles / C, r = a.tiles - R * C;
     a.split = 1;
     if (r > 0) {
