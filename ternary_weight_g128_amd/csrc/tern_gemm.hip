@@ -285,6 +285,11 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
 #pragma unroll
             for (int j = 0; j < 2; ++j) cw[j] = *reinterpret_cast<const u32x4_t *>(cur + c_lds + 32 * 32 * j);
             const unsigned char *ap = cur + a_row;
+            // activation operands one step ahead of the MFMAs that use them
+            bf16x8_t aop[kGemmMI], anx[kGemmMI];
+#pragma unroll
+            for (int i = 0; i < kGemmMI; ++i)
+                aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes + 16 * a_sw);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (q == 2) {
@@ -298,11 +303,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kappa = 2 * q + h;
-                    bf16x8_t aop[kGemmMI];
+                    if (kappa < 7) {
 #pragma unroll
-                    for (int i = 0; i < kGemmMI; ++i)
-                        aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
-                                                                     16 * (a_sw ^ kappa));
+                        for (int i = 0; i < kGemmMI; ++i)
+                            anx[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
+                                                                         16 * (a_sw ^ (kappa + 1)));
+                    }
                     bf16x8_t bop[2];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) bop[j] = operand_from_planes(t[j], h);
@@ -314,6 +320,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
                             // Horner step after each tile's last product of the group
                             if (kappa == 7) T[i][j] *= r[j];
                         }
+                    if (kappa < 7) {
+#pragma unroll
+                        for (int i = 0; i < kGemmMI; ++i) aop[i] = anx[i];
+                    }
                 }
             }
 #pragma unroll
