@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="rotated",
-                   choices=["rotated", "sweep", "prefill", "copy", "all"],
+                   choices=["rotated", "sweep", "prefill", "chain", "copy", "all"],
                    help="rotated: the headline step; sweep / prefill: extra measurements; "
                         "copy: a plain device copy of known size (counter calibration)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -290,6 +290,57 @@ def bench_prefill(tern, torch, synth, steps):
     return out
 
 
+def bench_chain(tern, torch, synth, passes=5):
+    """The 27B-class decode weight pass: 64 blocks of five chained GEMVs plus
+    the LM head (321 dependent launches), M=1, bf16 activations.  Where the
+    lengths match, a link's output (bf16) is the next link's input; the
+    6144-wide input of each block's second link is a fixed seeded vector.
+    Weights are drawn and packed on the GPU (6.49 GB resident).  `passes`
+    full passes are captured in one HIP graph and timed."""
+    gen = synth.device_generator(20)
+    links = synth.chain_links()
+    weights = []
+    for (K, N) in links:
+        codes = torch.empty((N, K // 16), dtype=torch.int32, device="cuda")
+        rows = max(1, (64 << 20) // K)
+        for n0 in range(0, N, rows):
+            nr = min(rows, N - n0)
+            tern.tern_pack_device(synth.device_ternary(gen, nr, K), out=codes[n0:n0 + nr])
+        s = synth.device_scales_f16(gen, N, K).view(torch.int16)
+        weights.append((codes, s))
+    x5120 = synth.device_activations_bf16(gen, 1, 5120)
+    x6144 = synth.device_activations_bf16(gen, 1, 6144)
+    cur = torch.empty((1, 5120), dtype=torch.bfloat16, device="cuda")
+    h5120 = torch.empty((1, 5120), dtype=torch.bfloat16, device="cuda")
+    qkv = torch.empty((1, 12288), dtype=torch.bfloat16, device="cuda")
+    gate = torch.empty((1, 17408), dtype=torch.bfloat16, device="cuda")
+    up = torch.empty((1, 17408), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((1, synth.LM_HEAD[1]), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def one_pass(_i):
+        cur.copy_(x5120)
+        for b in range(synth.CHAIN_BLOCKS):
+            w = weights[5 * b: 5 * b + 5]
+            tern.tern_gemv(cur, *w[0], out=qkv)           # 5120 -> 12288
+            tern.tern_gemv(x6144, *w[1], out=h5120)       # 6144 -> 5120 (fixed input)
+            tern.tern_gemv(h5120, *w[2], out=gate)        # 5120 -> 17408
+            tern.tern_gemv(h5120, *w[3], out=up)          # 5120 -> 17408
+            tern.tern_gemv(up, *w[4], out=cur)            # 17408 -> 5120
+        tern.tern_gemv(cur, *weights[-1], out=logits)     # LM head
+
+    one_pass(0)
+    torch.cuda.synchronize()
+    ms, _ = time_graph(torch, one_pass, passes)
+    ms_pass = ms / passes
+    packed = sum(tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K) for (K, N) in links)
+    act = sum(2 * K + (4 if i == len(links) - 1 else 2) * N for i, (K, N) in enumerate(links))
+    return {"gemvs": len(links), "packed_bytes": packed, "activation_bytes": act,
+            "ms_per_pass": ms_pass, "tokens_per_s": 1e3 / ms_pass,
+            "GB/s": (packed + act) / (ms_pass * 1e-3) / 1e9,
+            "frac_hbm": (packed + act) / (ms_pass * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -309,6 +360,9 @@ def main():
     if args.workload in ("sweep", "prefill"):
         fn = bench_sweep if args.workload == "sweep" else bench_prefill
         print(json.dumps({args.workload: fn(tern, torch, synth, args.steps)}))
+        return
+    if args.workload == "chain":
+        print(json.dumps({"chain": bench_chain(tern, torch, synth)}))
         return
 
     w, host, res = bench_rotated(args, tern, torch, synth)
@@ -336,6 +390,7 @@ def main():
         line["secondary"] = {
             "decode_sweep_gemv": bench_sweep(tern, torch, synth, 200),
             "prefill_gemm": bench_prefill(tern, torch, synth, 20),
+            "decode_pass_27b_class": bench_chain(tern, torch, synth),
         }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, host)

@@ -121,6 +121,14 @@ tern_status tern_dequant_f32(const uint32_t *codes, const uint16_t *s_f16,
  * Device operations.  Device pointers; enqueued on `stream`.
  * ------------------------------------------------------------------------ */
 
+/* Device-side packer (same slot format as tern_pack, "Memory requirement"):
+ * t[N][K] int8 on the device, each -1, 0 or +1, into codes[N][K/16].  Values
+ * are not checked: anything outside {-1, 0, 1} gives unspecified slots (use
+ * tern_pack on the host for validated packing).  Scales need no packing.
+ * t 16-byte aligned, codes 4-byte aligned, K a multiple of 128.
+ * Errors: TERN_EINVAL, TERN_EDEVICE. */
+tern_status tern_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream);
+
 /* Signed normalized Walsh-Hadamard transform along the last dimension, over
  * contiguous blocks of `block` elements ("Ternary-Bonsai-2-9B-2bit",
  * section 3), in natural Sylvester order H[i][l] = (-1)^popcount(i & l):

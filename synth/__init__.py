@@ -152,3 +152,33 @@ def make_problem(w: Workload, seed: int) -> Problem:
         x = activations_bf16(seed, w.M, w.K, w.outlier_frac)
     d = signs(seed, w.K) if w.rotate_block else None
     return Problem(t, s, x, d, {"workload": w.name, "seed": seed})
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws for workloads too large to generate on the host (the
+# 27B-class pass: 24.4 G weights).  Same distributions; torch's seeded CUDA
+# generator instead of PCG64.  Generation only: packing happens elsewhere.
+# ---------------------------------------------------------------------------
+
+def device_generator(seed: int):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def device_ternary(gen, rows: int, K: int):
+    """int8 [rows, K] on the GPU, i.i.d. uniform over {-1, 0, +1}."""
+    import torch
+    return torch.randint(-1, 2, (rows, K), dtype=torch.int8, device="cuda", generator=gen)
+
+
+def device_scales_f16(gen, N: int, K: int):
+    """binary16 scales [N, K/128] on the GPU: |N(0, 0.02)| + 1e-3."""
+    import torch
+    return (torch.randn((N, K // 128), device="cuda", generator=gen).abs_() * 0.02 + 1e-3).half()
+
+
+def device_activations_bf16(gen, M: int, K: int):
+    import torch
+    return torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)

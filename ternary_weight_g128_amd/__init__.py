@@ -26,7 +26,8 @@ TERN_FWHT_MAX_BLOCK = 4096
 EXPORTED = [
     "tern_abi_version", "tern_status_str", "tern_last_error", "tern_codes_bytes",
     "tern_scales_bytes", "tern_pack", "tern_pack_f32", "tern_unpack", "tern_dequant_f32",
-    "tern_fwht", "tern_gemv", "tern_rotate_gemv", "tern_gemm_workspace_bytes", "tern_gemm",
+    "tern_pack_device", "tern_fwht", "tern_gemv", "tern_rotate_gemv", "tern_gemm_workspace_bytes",
+    "tern_gemm",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -50,6 +51,7 @@ _lib.tern_pack.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.tern_pack_f32.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.tern_unpack.argtypes = [_P, _I64, _I64, _P]
 _lib.tern_dequant_f32.argtypes = [_P, _P, _I64, _I64, _P]
+_lib.tern_pack_device.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.tern_fwht.argtypes = [_P, _I, _P, _I64, _I64, _I64, _I, _P, _P]
 _lib.tern_gemv.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
 _lib.tern_rotate_gemv.argtypes = [_P, _I, _P, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P]
@@ -182,6 +184,17 @@ def _dev_ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def tern_pack_device(t, out=None, stream=None):
+    """t: int8 [N, K] on the GPU, values in {-1, 0, 1} (not checked) ->
+    codes int32 [N, K/16] (bit patterns of the uint32 words)."""
+    torch = _torch()
+    N, K = t.shape
+    if out is None:
+        out = torch.empty((N, K // 16), dtype=torch.int32, device=t.device)
+    _check(_lib.tern_pack_device(_dev_ptr(t), N, K, _dev_ptr(out), _stream_ptr(stream)), "tern_pack_device")
+    return out
 
 
 def tern_fwht(x, signs, block: int, inverse: bool = False, out=None, stream=None):

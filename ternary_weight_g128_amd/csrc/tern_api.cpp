@@ -171,6 +171,32 @@ tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32
         "tern_gemm");
 }
 
+tern_status tern_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream)
+{
+    if (N < 0 || K < 0) {
+        set_error("tern_pack_device: negative size");
+        return TERN_EINVAL;
+    }
+    if (K % TERN_GROUP != 0) {
+        set_error("tern_pack_device: K must be a multiple of 128");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!t || !codes) {
+        set_error("tern_pack_device: NULL pointer");
+        return TERN_EINVAL;
+    }
+    if (!aligned(t, 16) || !aligned(codes, 4)) {
+        set_error("tern_pack_device: t must be 16-byte aligned, codes 4-byte aligned");
+        return TERN_EINVAL;
+    }
+    if (N * (K / 16) >= ((int64_t)1 << 40)) {
+        set_error("tern_pack_device: matrix too large");
+        return TERN_EINVAL;
+    }
+    return device_status(tern::launch_pack_device(t, N, K, codes, stream), "tern_pack_device");
+}
+
 tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, int64_t K,
                       int64_t block, int inverse, float *y, void *stream)
 {

@@ -29,6 +29,7 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes,
                 const uint16_t *scales, int64_t N, float *y, void *workspace,
                 size_t workspace_bytes, void *stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int launch_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream);
 int64_t gemm_max_k();
 
 const char *hip_error_string(int err);

@@ -819,9 +819,41 @@ inline int gemv_rows_per_launch(int64_t N, int64_t K, bool x_f32)
     return 1;
 }
 
+// ---------------------------------------------------------------------------
+// Device packer: int8 t in {-1, 0, +1} -> 2-bit slots q = t + 1
+// ---------------------------------------------------------------------------
+// One thread per code word: a 16-byte load of the word's 16 weights, slot j
+// of the word at bits 2j..2j + 1.  Values outside {-1, 0, 1} are not checked
+// (their slots are unspecified).
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t *__restrict__ t, uint32_t *__restrict__ codes,
+                                                   int64_t words)
+{
+    for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < words; w += (int64_t)gridDim.x * 256) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + 16 * w);
+        uint32_t code = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int tv = (int8_t)((v[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            code |= (uint32_t)((tv + 1) & 3) << (2 * j);
+        }
+        codes[w] = code;
+    }
+}
+
 }  // namespace
 
 namespace tern {
+
+int launch_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream)
+{
+    const int64_t words = N * (K / 16);
+    if (words == 0) return 0;
+    const int64_t blocks = (words + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), t, codes, words);
+    return (int)hipGetLastError();
+}
+
 
 const char *hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
 

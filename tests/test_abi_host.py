@@ -126,6 +126,24 @@ def test_rotate_gemv_rejects(tern, kw, status):
     assert _rot(tern, **kw) == status
 
 
+def _packd(tern, t=A16, N=4, K=128, codes=A16):
+    return tern.lib().tern_pack_device(t, N, K, codes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), 1), (dict(N=-1), 1), (dict(t=NULL), 1), (dict(codes=NULL), 1),
+    (dict(t=A2), 1), (dict(codes=A2), 1),
+])
+def test_pack_device_rejects(tern, kw, status):
+    assert _packd(tern, **kw) == status
+    assert tern.tern_last_error().startswith("tern_pack_device")
+
+
+def test_pack_device_empty_is_noop(tern):
+    assert _packd(tern, N=0, t=NULL, codes=NULL) == 0
+    assert _packd(tern, K=0, t=NULL, codes=NULL) == 0
+
+
 def test_codec_rejects(tern):
     t = np.zeros((2, 128), dtype=np.int8)
     t[1, 5] = 2

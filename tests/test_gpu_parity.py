@@ -451,6 +451,17 @@ def test_gemm_k_zero_and_empty(tern):
     T.cuda.synchronize()
 
 
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (33, 1280), (1000, 5120)])
+def test_pack_device_matches_oracle_encode(tern, oracle_lib, N, K):
+    """Device packer: bit-exact against the oracle's encoder."""
+    T = torch()
+    t = synth.ternary(60 + N + K, N, K)
+    codes = tern.tern_pack_device(T.from_numpy(t).cuda())
+    T.cuda.synchronize()
+    ref = oracle_lib.encode(t)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32), ref)
+
+
 # ---------------------------------------------------------------------------
 # HIP graph capture of the decode step: every replay equals eager execution
 # ---------------------------------------------------------------------------
