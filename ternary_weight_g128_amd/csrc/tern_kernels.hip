@@ -701,23 +701,22 @@ struct GemvPlan {
     size_t lds;
 };
 
-// Tiles per wave and the split of a workgroup's waves between tiles (wt)
-// and K (wk).  Large N: waves take different tiles over all of K (no
-// reduction; the staged activations serve wt * TPW tiles).  Small N: waves
-// split K of the same tiles so that there are enough waves in flight (about
-// 2048 in total), each with at least two 256-K blocks.
+// Tiles per wave and the split of a workgroup's four waves between tiles
+// (wt) and K (wk), from a sweep of the decode shapes on MI355X: one tile per
+// wave, except two when the staged activations of a workgroup are large
+// (then fewer workgroups stage them); two tile-waves x two K-waves for many
+// tiles, otherwise four K-waves (each with at least two 256-K blocks).
 inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
 {
     const int64_t tiles = (N + kTileN - 1) / kTileN;
     const int nblk = (int)((K / kGroup + 1) / 2);
     GemvPlan pl;
-    pl.tpw = (mx <= 4 && tiles >= 4096) ? 2 : ((tiles + 1) / 2 >= 512 ? 2 : 1);
+    pl.tpw = K * mx * 2 >= 96 * 1024 ? 2 : 1;
     const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
-    pl.wt = 1;
-    while (pl.wt < 4 && tile_groups / (pl.wt * 2) >= 1024) pl.wt *= 2;
+    pl.wt = tile_groups >= 1024 ? 2 : 1;
+    pl.wk = 4 / pl.wt;
+    while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
     pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
-    pl.wk = 1;
-    while (pl.wt * pl.wk < 8 && pl.wgs * pl.wt * pl.wk < 2048 && nblk >= 4 * pl.wk) pl.wk *= 2;
     const int waves = pl.wt * pl.wk;
     pl.lds = (size_t)K * mx * 2 + (size_t)waves * pl.tpw * mx * kTileN * sizeof(float);
     return pl;
