@@ -462,6 +462,40 @@ def test_pack_device_matches_oracle_encode(tern, oracle_lib, N, K):
     assert np.array_equal(codes.cpu().numpy().view(np.uint32), ref)
 
 
+def test_chained_block_links(tern, oracle_lib):
+    """One block of the 27B-class decode pass at full size, chained the way
+    the benchmark chains it (bf16 outputs feed the next link where lengths
+    match); every link is checked on sampled rows against the oracle on the
+    bf16 input it actually received."""
+    T = torch()
+    links = synth.CHAIN_BLOCK
+    w = []
+    for li, (K, N) in enumerate(links):
+        seed = 900 + li
+        rows = sampled_rows(N, 12, seed)
+        codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, N, K, 1.0 / 3.0, rows)
+        w.append((codes_d, scales_d, t_rows, s_rows, rows, K, N))
+    x5120 = x_to_device(synth.activations_bf16(950, 1, 5120))
+    x6144 = x_to_device(synth.activations_bf16(951, 1, 6144))
+
+    def run(li, xin):
+        codes_d, scales_d, t_rows, s_rows, rows, K, N = w[li]
+        y = tern.tern_gemv(xin, codes_d, scales_d, out_dtype=T.bfloat16)
+        T.cuda.synchronize()
+        xh = xin.view(T.int16).cpu().numpy().view(np.uint16)
+        y_ref, bound = oracle_lib.matmul(xh, oracle_lib.encode(t_rows), s_rows, K)
+        assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound, bf16_out=True,
+                            what=f"chain link {li} ({K}->{N})")
+        return y
+
+    run(0, x5120)              # 5120 -> 12288
+    h = run(1, x6144)          # 6144 -> 5120
+    run(2, h)                  # 5120 -> 17408 (gate)
+    up = run(3, h)             # 5120 -> 17408 (up)
+    out = run(4, up)           # 17408 -> 5120 (down): the next block's input
+    assert out.shape == (1, 5120) and T.isfinite(out.float()).all()
+
+
 # ---------------------------------------------------------------------------
 # HIP graph capture of the decode step: every replay equals eager execution
 # ---------------------------------------------------------------------------
