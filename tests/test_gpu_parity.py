@@ -534,3 +534,56 @@ def test_rotated_step_graph_replays_match_eager(tern):
         assert T.equal(y, y_eager), f"replay {r}"
         step()                      # eager work between replays
         T.cuda.synchronize()
+
+
+def test_gemm_graph_replays_match_eager(tern):
+    """tern_gemm with split tiles (workspace + fixup pass) captured in a HIP
+    graph: every replay, with eager work in between, equals the eager call."""
+    T = torch()
+    M, K, N, seed = 600, 4096, 700, 41
+    assert tern.tern_gemm_workspace_bytes(M, N, K) > 0  # the split path
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    xd = x_to_device(synth.activations_bf16(seed, M, K, outlier_frac=0.01))
+    y = T.empty((M, N), dtype=T.float32, device="cuda")
+    ws = T.empty(tern.tern_gemm_workspace_bytes(M, N, K), dtype=T.uint8, device="cuda")
+    tern.tern_gemm(xd, codes_d, scales_d, out=y, workspace=ws)
+    T.cuda.synchronize()
+    y_eager = y.clone()
+    g = T.cuda.CUDAGraph()
+    st = T.cuda.Stream()
+    st.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(st):
+        with T.cuda.graph(g, stream=st):
+            tern.tern_gemm(xd, codes_d, scales_d, out=y, workspace=ws)
+    T.cuda.current_stream().wait_stream(st)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xFF)                      # stale workspace contents must not matter
+        other = T.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, y_eager), f"replay {rep} differs"
+        assert T.isfinite(other)
+
+
+@pytest.mark.parametrize("b", [64, 4096])
+def test_rotation_fold_into_weight_rows(tern, b):
+    """Folding the rotation into the weights: with W' = rows of W transformed
+    forward and x' = the forward transform of x, W' x' = W x (H is symmetric,
+    H H = b I, D D = I).  Dense fp32 weights, checked against fp64."""
+    T = torch()
+    rng = np.random.default_rng(b)
+    N, K = 96, 2 * b
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    d = synth.signs(b, K)
+    dd = T.from_numpy(d).cuda()
+    Wf = tern.tern_fwht(T.from_numpy(W).cuda(), dd, b)
+    xf = tern.tern_fwht(T.from_numpy(x).cuda(), dd, b)
+    T.cuda.synchronize()
+    y_fold = xf.double().cpu().numpy() @ Wf.double().cpu().numpy().T
+    y_ref = x.astype(np.float64) @ W.astype(np.float64).T
+    scale = np.abs(x).astype(np.float64) @ np.abs(W).astype(np.float64).T
+    assert np.all(np.abs(y_fold - y_ref) <= 1e-5 * scale)
