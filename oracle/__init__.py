@@ -63,6 +63,13 @@ def lib():
         L.oracle_ternary_from_f32.argtypes = [P, I64, I64, P, P]
         L.oracle_bits_per_weight.argtypes = [I64, I64]
         L.oracle_bits_per_weight.restype = ctypes.c_double
+        L.oracle_dequant_g64.argtypes = [P, P, I64, I64, P]
+        L.oracle_dequant_affine.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, I64, I64, P]
+        L.oracle_b1_decode.argtypes = [P, I64, I64, P]
+        L.oracle_b1_decode.restype = None
+        L.oracle_b1_encode.argtypes = [P, I64, I64, P]
+        L.oracle_format_bits_per_weight.argtypes = [ctypes.c_int, I64, I64]
+        L.oracle_format_bits_per_weight.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -221,3 +228,63 @@ def dequant(codes: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     t = decode(codes, K).astype(np.float64)
     s = half_bits_to_f64(scales)
     return t * np.repeat(s, 128, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# format variants (group-64 scales, affine scale+bias container, binary g128)
+# ---------------------------------------------------------------------------
+
+FMT_G128, FMT_G64, FMT_AFFINE2, FMT_B1, FMT_AFFINE1 = 0, 1, 2, 3, 4
+
+
+def format_bits_per_weight(fmt: int, N: int, K: int) -> float:
+    return lib().oracle_format_bits_per_weight(fmt, N, K)
+
+
+def dequant_g64(codes: np.ndarray, s64: np.ndarray, K: int) -> np.ndarray:
+    """Dense float64 weights of the group-64 variant: same slot codes, the
+    scale of weight k is s64[n][k / 64]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    s64 = np.ascontiguousarray(s64, dtype=np.uint16)
+    N = codes.shape[0]
+    assert s64.shape == (N, K // 64)
+    w = np.zeros((N, K), dtype=np.float64)
+    if lib().oracle_dequant_g64(_ptr(codes), _ptr(s64), N, K, _ptr(w)):
+        raise ValueError("slot value 3 is not a ternary code")
+    return w
+
+
+def dequant_affine(words: np.ndarray, bits: int, group: int, scales: np.ndarray,
+                   biases: np.ndarray, K: int) -> np.ndarray:
+    """Dense float64 weights scale * q + bias of the affine group format with
+    `bits`-bit fields (1 or 2), lowest field first in each uint32."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    N = words.shape[0]
+    assert words.shape == (N, K * bits // 32)
+    assert scales.shape == biases.shape == (N, K // group)
+    w = np.zeros((N, K), dtype=np.float64)
+    if lib().oracle_dequant_affine(_ptr(words), bits, group, _ptr(scales), _ptr(biases), N, K, _ptr(w)):
+        raise ValueError("unsupported affine format")
+    return w
+
+
+def b1_decode(bits: np.ndarray, K: int) -> np.ndarray:
+    """uint32 bit words [N, K/32] -> int8 b [N, K] in {-1, +1} (bit 1 is +1)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    N = bits.shape[0]
+    b = np.zeros((N, K), dtype=np.int8)
+    lib().oracle_b1_decode(_ptr(bits), N, K, _ptr(b))
+    return b
+
+
+def b1_encode(b: np.ndarray) -> np.ndarray:
+    """int8 b [N, K] in {-1, +1} -> uint32 bit words [N, K/32]."""
+    b = np.ascontiguousarray(b, dtype=np.int8)
+    N, K = b.shape
+    assert K % 32 == 0
+    bits = np.zeros((N, K // 32), dtype=np.uint32)
+    if lib().oracle_b1_encode(_ptr(b), N, K, _ptr(bits)):
+        raise ValueError("not binary")
+    return bits

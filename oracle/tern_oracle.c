@@ -251,3 +251,93 @@ double oracle_bits_per_weight(int64_t N, int64_t K)
     double scale_bytes = 2.0 * (double)N * (double)K / ORACLE_GROUP;
     return 8.0 * (code_bytes + scale_bytes) / ((double)N * (double)K);
 }
+
+/* ------------------------------------------------------------------------
+ * Format variants ([MC] "Shipped components", "MLX packaging", and the
+ * 1-bit row of the variant table under "Benchmarks").  Each is written as
+ * its dequantized value, so that a transcode can be checked by comparing
+ * dense weights.
+ * --------------------------------------------------------------------- */
+
+/* Group-size-64 variant ([MC] Shipped components): the same 2-bit slot codes;
+ * the FP16 scale of weight k of row n is s64[n][k/64].  Dense w[N][K] in
+ * double.  Returns 0, or 3 if a slot holds 3. */
+int oracle_dequant_g64(const uint32_t *codes, const uint16_t *s64, int64_t N, int64_t K, double *w)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int t;
+            if (slot_t(codes, K, n, k, &t)) return 3;
+            w[n * K + k] = oracle_half_to_double(s64[n * (K / 64) + k / 64]) * (double)t;
+        }
+    return 0;
+}
+
+/* Affine group format with a scale and a bias per group ([MC] MLX packaging):
+ * unsigned fields of `bits` bits (1 or 2), 32/bits of them per little-endian
+ * uint32 word, lowest field first, K-major per row; one FP16 (scale, bias)
+ * pair per `group` consecutive K; the weight is scale * q + bias, evaluated in
+ * double.  Returns 0, or 1 for unsupported bits/group. */
+int oracle_dequant_affine(const uint32_t *words, int bits, int group, const uint16_t *scales,
+                          const uint16_t *biases, int64_t N, int64_t K, double *w)
+{
+    if ((bits != 1 && bits != 2) || group <= 0 || K % group != 0 || (K * bits) % 32 != 0) return 1;
+    const int64_t per_word = 32 / bits, wpr = K / per_word, gpr = K / group;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t word = words[n * wpr + k / per_word];
+            double q = (double)((word >> (bits * (k % per_word))) & mask);
+            double scale = oracle_half_to_double(scales[n * gpr + k / group]);
+            double bias = oracle_half_to_double(biases[n * gpr + k / group]);
+            w[n * K + k] = scale * q + bias;
+        }
+    return 0;
+}
+
+/* Binary g128 variant ([MC] Benchmarks: the 1-bit model, 1.125 bits/weight =
+ * one bit plus an FP16 scale per 128): bit j of word w of row n holds weight
+ * k = 32 w + j, 1 for +1 and 0 for -1 (little-endian uint32, lowest bit
+ * first).  Decode into b in {-1, +1}. */
+void oracle_b1_decode(const uint32_t *bits, int64_t N, int64_t K, int8_t *b)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t bit = (bits[n * (K / 32) + k / 32] >> (k % 32)) & 1u;
+            b[n * K + k] = bit ? (int8_t)1 : (int8_t)-1;
+        }
+}
+
+/* Encode b in {-1, +1} as above.  Returns 0, or 2 if some b is not +-1. */
+int oracle_b1_encode(const int8_t *b, int64_t N, int64_t K, uint32_t *bits)
+{
+    for (int64_t i = 0; i < N * (K / 32); ++i) bits[i] = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int v = b[n * K + k];
+            if (v != 1 && v != -1) return 2;
+            if (v == 1) bits[n * (K / 32) + k / 32] |= 1u << (k % 32);
+        }
+    return 0;
+}
+
+/* Storage of each format in bits per weight, from its byte counts:
+ *   0  ternary g128, 2-bit slots + FP16 scale per 128   ([MC] Memory requirement)
+ *   1  ternary, 2-bit slots + FP16 scale per 64          ([MC] Shipped components)
+ *   2  2-bit fields + FP16 scale and FP16 bias per 128   ([MC] MLX packaging)
+ *   3  binary g128, 1 bit + FP16 scale per 128           ([MC] Benchmarks, 1-bit row)
+ *   4  1-bit fields + FP16 scale and FP16 bias per 128   (affine container of format 3)
+ * Returns -1 for an unknown format. */
+double oracle_format_bits_per_weight(int format, int64_t N, int64_t K)
+{
+    double nk = (double)N * (double)K, field_bytes, side_bytes;
+    switch (format) {
+    case 0: field_bytes = nk / 4.0; side_bytes = 2.0 * nk / 128.0; break;
+    case 1: field_bytes = nk / 4.0; side_bytes = 2.0 * nk / 64.0; break;
+    case 2: field_bytes = nk / 4.0; side_bytes = 4.0 * nk / 128.0; break;
+    case 3: field_bytes = nk / 8.0; side_bytes = 2.0 * nk / 128.0; break;
+    case 4: field_bytes = nk / 8.0; side_bytes = 4.0 * nk / 128.0; break;
+    default: return -1.0;
+    }
+    return 8.0 * (field_bytes + side_bytes) / nk;
+}

@@ -405,3 +405,108 @@ def test_pages_accounting_relations():
     assert 2 + 32 / 128 == g["mlx_bits_per_weight"]
     assert 1 + 16 / 128 == g["binary_bits_per_weight"]
     assert round(2.125 / 1.125, 1) == g["ternary_vs_binary_bytes_ratio"]
+
+
+# ---------------------------------------------------------------------------
+# format variants: group-64 scales, affine (scale, bias) container, binary g128
+# ---------------------------------------------------------------------------
+
+def _np_pack_fields(q, bits):
+    """Pack unsigned fields q [N, K] (each < 2^bits) lowest-first into uint32
+    words, written with numpy shifts only."""
+    N, K = q.shape
+    per = 32 // bits
+    q = q.astype(np.uint64).reshape(N, K // per, per)
+    shifts = (np.arange(per, dtype=np.uint64) * bits)[None, None, :]
+    return (q << shifts).sum(axis=2).astype(np.uint32)
+
+
+def test_format_bits_per_weight_pages(oracle_lib):
+    g = _golden()
+    for N, K in [(1, 128), (17408, 5120), (248320, 5120)]:
+        assert oracle_lib.format_bits_per_weight(oracle_lib.FMT_G128, N, K) == g["deployed_bits_per_weight"]
+        assert oracle_lib.format_bits_per_weight(oracle_lib.FMT_AFFINE2, N, K) == g["mlx_bits_per_weight"]
+        assert oracle_lib.format_bits_per_weight(oracle_lib.FMT_B1, N, K) == g["binary_bits_per_weight"]
+        assert oracle_lib.format_bits_per_weight(oracle_lib.FMT_G64, N, K) == 2.25
+        assert oracle_lib.format_bits_per_weight(oracle_lib.FMT_AFFINE1, N, K) == 1.25
+    # the two shipped ternary packages hold the same weights
+    n128 = g["g128_package_gb"] * 8 / oracle_lib.format_bits_per_weight(oracle_lib.FMT_G128, 1, 128)
+    n64 = g["g64_package_gb"] * 8 / oracle_lib.format_bits_per_weight(oracle_lib.FMT_G64, 1, 128)
+    assert abs(n128 - n64) / n128 < 0.002
+    b1 = oracle_lib.format_bits_per_weight(oracle_lib.FMT_B1, 1, 128)
+    assert round(2.125 / b1, 1) == g["ternary_vs_binary_bytes_ratio"]
+    assert oracle_lib.format_bits_per_weight(9, 1, 128) == -1.0
+
+
+def test_dequant_g64_is_repeated_g128(oracle_lib):
+    rng = np.random.default_rng(61)
+    N, K = 5, 512
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    s128 = synth.scales_f16(611, N, K)
+    codes = oracle_lib.encode(t)
+    dense = t.astype(np.float64) * np.repeat(oracle_lib.half_bits_to_f64(s128), 128, axis=1)
+    s64 = np.repeat(s128, 2, axis=1)
+    assert np.array_equal(oracle_lib.dequant_g64(codes, s64, K), dense)
+    # distinct halves: weight k takes the scale of its own 64-block
+    s64b = synth.scales_f16(612, N, 2 * K)
+    dense_b = t.astype(np.float64) * np.repeat(oracle_lib.half_bits_to_f64(s64b), 64, axis=1)
+    assert np.array_equal(oracle_lib.dequant_g64(codes, s64b, K), dense_b)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 128), (2, 64), (1, 128), (1, 32)])
+def test_dequant_affine_closed_form(oracle_lib, bits, group):
+    rng = np.random.default_rng(62 + bits + group)
+    N, K = 4, 256
+    q = rng.integers(0, 1 << bits, size=(N, K))
+    words = _np_pack_fields(q, bits)
+    sc = synth.scales_f16(621, N, K * 128 // group)
+    bi = synth.scales_f16(622, N, K * 128 // group) | np.uint16(0x8000)
+    want = (q.astype(np.float64) * np.repeat(oracle_lib.half_bits_to_f64(sc), group, axis=1)
+            + np.repeat(oracle_lib.half_bits_to_f64(bi), group, axis=1))
+    assert np.array_equal(oracle_lib.dequant_affine(words, bits, group, sc, bi, K), want)
+
+
+def test_affine_pairs_reading_of_the_mlx_packaging(oracle_lib):
+    """The pair (2 s, -s) gives exactly +-s on one-bit fields, as the MLX
+    packaging section says, but no zero level on 2-bit fields; the pair
+    (s, -s) on the 2-bit slots q = t + 1 gives exactly s * t."""
+    rng = np.random.default_rng(63)
+    N, K = 3, 256
+    s = synth.scales_f16(631, N, K)                      # positive FP16
+    sd = oracle_lib.half_bits_to_f64(s)
+    two_s = np.array([[np.float16(2.0 * v) for v in row] for row in sd], dtype=np.float16).view(np.uint16)
+    neg_s = s | np.uint16(0x8000)
+    b = rng.choice(np.array([-1, 1], dtype=np.int8), size=(N, K))
+    bits = oracle_lib.b1_encode(b)
+    w1 = oracle_lib.dequant_affine(bits, 1, 128, two_s, neg_s, K)
+    assert np.array_equal(w1, b * np.repeat(sd, 128, axis=1))
+    q_all = np.tile(np.arange(4), (N, K // 4))
+    w2 = oracle_lib.dequant_affine(_np_pack_fields(q_all, 2), 2, 128, two_s, neg_s, K)
+    levels = np.repeat(sd, 128, axis=1)
+    assert np.array_equal(w2, (2 * q_all - 1) * levels)  # -s, s, 3s, 5s
+    assert not np.any(w2 == 0)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    w3 = oracle_lib.dequant_affine(oracle_lib.encode(t), 2, 128, s, neg_s, K)
+    assert np.array_equal(w3, t * levels)
+
+
+def test_b1_decode_all_patterns_of_sixteen_bits(oracle_lib):
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    for shift in (0, 16):
+        words = np.zeros((pats.size, 4), dtype=np.uint32)      # K = 128
+        words[:, 2] = pats << shift
+        b = oracle_lib.b1_decode(words, 128)
+        idx = np.arange(16)
+        want = np.where(((pats[:, None] >> idx[None, :]) & 1) == 1, 1, -1)
+        assert np.array_equal(b[:, 64 + shift: 64 + shift + 16], want)
+        others = np.delete(np.arange(128), np.arange(64 + shift, 80 + shift))
+        assert np.all(b[:, others] == -1)
+        assert np.array_equal(oracle_lib.b1_encode(b), words)
+
+
+def test_b1_encode_rejects_non_binary(oracle_lib):
+    for bad in (0, 2, -2):
+        b = np.ones((2, 128), dtype=np.int8)
+        b[1, 77] = bad
+        with pytest.raises(ValueError):
+            oracle_lib.b1_encode(b)
