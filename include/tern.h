@@ -118,6 +118,83 @@ tern_status tern_dequant_f32(const uint32_t *codes, const uint16_t *s_f16,
                              int64_t N, int64_t K, float *w);
 
 /* ---------------------------------------------------------------------------
+ * Format variants ("prism-ml/Ternary-Bonsai-27B-mlx-2bit" model card).
+ * Host pointers, caller-owned, synchronous; K a multiple of 128 throughout.
+ * Each variant converts to and from the g128 slot format exactly, so the
+ * device kernels above serve all of them.
+ * ------------------------------------------------------------------------ */
+
+/* Group-size-64 variant ("Shipped components"): the same codes, with each
+ * g128 scale repeated for both 64-value halves of its group; 2.25 bits per
+ * weight.  Scale array [N][K/64]. */
+size_t tern_scales_g64_bytes(int64_t N, int64_t K);  /* 2*N*K/64 */
+
+/* s[N][K/128] -> s64[N][K/64], s64[n][2g] = s64[n][2g+1] = s[n][g].  s64 may
+ * start at s (in-place widening; the buffer must hold N*K/64 values).
+ * Errors: TERN_EINVAL (sizes, NULL). */
+tern_status tern_scales_to_g64(const uint16_t *s, int64_t N, int64_t K, uint16_t *s64);
+
+/* s64[N][K/64] -> s[N][K/128] (s may start at s64).  Every pair of halves must
+ * hold equal values (the first of the pair is kept): TERN_ENOTTERNARY if
+ * not, since such a matrix has no g128 form; TERN_EINVAL for a non-finite
+ * scale, bad sizes or NULL.  Nothing is written on error. */
+tern_status tern_scales_from_g64(const uint16_t *s64, int64_t N, int64_t K, uint16_t *s);
+
+/* Affine scale+bias container ("MLX packaging": a binary16 scale and bias per
+ * group of 128, weight = scale * q + bias, 2.25 bits per weight).  The 2-bit
+ * fields are the slot codes unchanged (q = t + 1, lowest field first), and a
+ * ternary group exports as (scale, bias) = (s, -s), so scale * q + bias =
+ * s * t exactly.  (The pair (2s, -s) that section prints has no zero level on
+ * 2-bit fields; it is the pair of the binary variant, tern_mlx_export_b1.)
+ * Outputs mlx_scales, mlx_biases [N][K/128].  Errors: TERN_EINVAL (sizes,
+ * NULL, a non-finite scale). */
+tern_status tern_mlx_export(const uint16_t *s, int64_t N, int64_t K,
+                            uint16_t *mlx_scales, uint16_t *mlx_biases);
+
+/* Inverse of tern_mlx_export: s = mlx_scales (s may equal mlx_scales).
+ * TERN_ENOTTERNARY if some group has bias != -scale (by value); TERN_EINVAL
+ * for non-finite values, bad sizes or NULL.  Nothing is written on error. */
+tern_status tern_mlx_import(const uint16_t *mlx_scales, const uint16_t *mlx_biases,
+                            int64_t N, int64_t K, uint16_t *s);
+
+/* Binary g128 variant (the 1-bit model of the "Benchmarks" variant table,
+ * 1.125 bits per weight): b in {-1, +1}, one bit per weight, bit j of word w
+ * of row n holds k = 32w + j (1 for +1, 0 for -1, lowest bit first), and the
+ * same binary16 scale per 128 as the ternary format.  Bit words [N][K/32]. */
+#define TERN_B1_PER_WORD 32
+size_t tern_b1_bytes(int64_t N, int64_t K);  /* N*K/8 */
+
+/* b[N][K] int8 (each -1 or +1) -> bits[N][K/32].
+ * Errors: TERN_EINVAL (sizes, NULL), TERN_ENOTTERNARY (a value not +-1;
+ * bits then undefined). */
+tern_status tern_pack_b1(const int8_t *b, int64_t N, int64_t K, uint32_t *bits);
+
+/* bits[N][K/32] -> b[N][K] in {-1, +1}.  Errors: TERN_EINVAL. */
+tern_status tern_unpack_b1(const uint32_t *bits, int64_t N, int64_t K, int8_t *b);
+
+/* Binary weights as ternary slot codes (t = b, so q = 2 * bit), for the
+ * g128 kernels: bits[N][K/32] -> codes[N][K/16]; the scales carry over
+ * unchanged.  Errors: TERN_EINVAL. */
+tern_status tern_b1_to_codes(const uint32_t *bits, int64_t N, int64_t K, uint32_t *codes);
+
+/* Ternary slot codes with no zero weight -> bits.  TERN_ENOTTERNARY if some
+ * t = 0 (no binary code), TERN_EBADCODE for slot value 3; bits then
+ * undefined.  Errors also TERN_EINVAL. */
+tern_status tern_codes_to_b1(const uint32_t *codes, int64_t N, int64_t K, uint32_t *bits);
+
+/* Affine container of the binary variant with 1-bit fields ("MLX packaging"
+ * pair): (scale, bias) = (2s, -s), so scale * bit + bias = +-s exactly; the
+ * bit words are used unchanged (1.25 bits per weight).  TERN_EINVAL if some
+ * |s| >= 32768 (2s overflows binary16) or is not finite. */
+tern_status tern_mlx_export_b1(const uint16_t *s, int64_t N, int64_t K,
+                               uint16_t *mlx_scales, uint16_t *mlx_biases);
+
+/* Inverse: s = -bias.  TERN_ENOTTERNARY if some group has scale != -2 * bias
+ * (by value); TERN_EINVAL for non-finite values, bad sizes or NULL. */
+tern_status tern_mlx_import_b1(const uint16_t *mlx_scales, const uint16_t *mlx_biases,
+                               int64_t N, int64_t K, uint16_t *s);
+
+/* ---------------------------------------------------------------------------
  * Device operations.  Device pointers; enqueued on `stream`.
  * ------------------------------------------------------------------------ */
 

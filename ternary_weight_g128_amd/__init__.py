@@ -27,8 +27,12 @@ EXPORTED = [
     "tern_abi_version", "tern_status_str", "tern_last_error", "tern_codes_bytes",
     "tern_scales_bytes", "tern_pack", "tern_pack_f32", "tern_unpack", "tern_dequant_f32",
     "tern_pack_device", "tern_fwht", "tern_gemv", "tern_rotate_gemv", "tern_gemm_workspace_bytes",
-    "tern_gemm",
+    "tern_gemm", "tern_scales_g64_bytes", "tern_scales_to_g64", "tern_scales_from_g64",
+    "tern_mlx_export", "tern_mlx_import", "tern_b1_bytes", "tern_pack_b1", "tern_unpack_b1",
+    "tern_b1_to_codes", "tern_codes_to_b1", "tern_mlx_export_b1", "tern_mlx_import_b1",
 ]
+_SIZE_FNS = ("tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes",
+             "tern_scales_g64_bytes", "tern_b1_bytes")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libtern.so is not built ({LIB_PATH}); run __graft_entry__.build()")
@@ -58,9 +62,18 @@ _lib.tern_rotate_gemv.argtypes = [_P, _I, _P, _I64, _I64, _I64, _P, _P, _I64, _P
 _lib.tern_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 _lib.tern_gemm_workspace_bytes.restype = _SZ
 _lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
+for _name in ("tern_scales_g64_bytes", "tern_b1_bytes"):
+    getattr(_lib, _name).argtypes = [_I64, _I64]
+    getattr(_lib, _name).restype = _SZ
+for _name in ("tern_scales_to_g64", "tern_scales_from_g64", "tern_pack_b1", "tern_unpack_b1",
+              "tern_b1_to_codes", "tern_codes_to_b1"):
+    getattr(_lib, _name).argtypes = [_P, _I64, _I64, _P]
+for _name in ("tern_mlx_export", "tern_mlx_export_b1"):
+    getattr(_lib, _name).argtypes = [_P, _I64, _I64, _P, _P]
+for _name in ("tern_mlx_import", "tern_mlx_import_b1"):
+    getattr(_lib, _name).argtypes = [_P, _P, _I64, _I64, _P]
 for _name in EXPORTED:
-    if _name not in ("tern_abi_version", "tern_status_str", "tern_last_error",
-                     "tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes"):
+    if _name not in ("tern_abi_version", "tern_status_str", "tern_last_error") + _SIZE_FNS:
         getattr(_lib, _name).restype = _I
 
 
@@ -150,6 +163,120 @@ def tern_dequant_f32(codes: np.ndarray, s_f16: np.ndarray, K: int) -> np.ndarray
     w = np.empty((N, K), dtype=np.float32)
     _check(_lib.tern_dequant_f32(_np_ptr(codes), _np_ptr(s), N, K, _np_ptr(w)), "tern_dequant_f32")
     return w
+
+
+# --------------------------------------------------------------------------
+# format variants (host)
+# --------------------------------------------------------------------------
+
+def tern_scales_g64_bytes(N: int, K: int) -> int:
+    return _lib.tern_scales_g64_bytes(N, K)
+
+
+def tern_b1_bytes(N: int, K: int) -> int:
+    return _lib.tern_b1_bytes(N, K)
+
+
+def _scales_arg(s: np.ndarray, per_group: int, name: str):
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    if s.ndim != 2:
+        raise ValueError(f"{name}: scales must be 2-D")
+    return s, s.shape[0], s.shape[1] * TERN_GROUP // per_group
+
+
+def tern_scales_to_g64(s: np.ndarray) -> np.ndarray:
+    """binary16 scale bits [N, K/128] -> [N, K/64], each scale repeated."""
+    s, N, K = _scales_arg(s, 1, "tern_scales_to_g64")
+    out = np.empty((N, K // 64), dtype=np.uint16)
+    _check(_lib.tern_scales_to_g64(_np_ptr(s), N, K, _np_ptr(out)), "tern_scales_to_g64")
+    return out
+
+
+def tern_scales_from_g64(s64: np.ndarray) -> np.ndarray:
+    """binary16 scale bits [N, K/64] with equal halves -> [N, K/128]."""
+    s64 = np.ascontiguousarray(s64, dtype=np.uint16)
+    N, K = s64.shape[0], s64.shape[1] * 64
+    if K % TERN_GROUP:
+        raise ValueError("tern_scales_from_g64: need an even number of 64-blocks per row")
+    out = np.empty((N, K // TERN_GROUP), dtype=np.uint16)
+    _check(_lib.tern_scales_from_g64(_np_ptr(s64), N, K, _np_ptr(out)), "tern_scales_from_g64")
+    return out
+
+
+def _mlx_export(fn, s, where):
+    s, N, K = _scales_arg(s, 1, where)
+    sc = np.empty_like(s)
+    bi = np.empty_like(s)
+    _check(fn(_np_ptr(s), N, K, _np_ptr(sc), _np_ptr(bi)), where)
+    return sc, bi
+
+
+def _mlx_import(fn, sc, bi, where):
+    sc, N, K = _scales_arg(sc, 1, where)
+    bi = np.ascontiguousarray(bi, dtype=np.uint16)
+    if bi.shape != sc.shape:
+        raise ValueError(f"{where}: scales and biases differ in shape")
+    s = np.empty_like(sc)
+    _check(fn(_np_ptr(sc), _np_ptr(bi), N, K, _np_ptr(s)), where)
+    return s
+
+
+def tern_mlx_export(s: np.ndarray):
+    """g128 scales -> (mlx_scales, mlx_biases) = (s, -s) for the 2-bit slots."""
+    return _mlx_export(_lib.tern_mlx_export, s, "tern_mlx_export")
+
+
+def tern_mlx_import(mlx_scales: np.ndarray, mlx_biases: np.ndarray) -> np.ndarray:
+    return _mlx_import(_lib.tern_mlx_import, mlx_scales, mlx_biases, "tern_mlx_import")
+
+
+def tern_mlx_export_b1(s: np.ndarray):
+    """binary-variant scales -> (mlx_scales, mlx_biases) = (2s, -s) for 1-bit fields."""
+    return _mlx_export(_lib.tern_mlx_export_b1, s, "tern_mlx_export_b1")
+
+
+def tern_mlx_import_b1(mlx_scales: np.ndarray, mlx_biases: np.ndarray) -> np.ndarray:
+    return _mlx_import(_lib.tern_mlx_import_b1, mlx_scales, mlx_biases, "tern_mlx_import_b1")
+
+
+def tern_pack_b1(b: np.ndarray) -> np.ndarray:
+    """int8 b [N, K] in {-1, +1} -> uint32 bit words [N, K/32]."""
+    b = np.ascontiguousarray(b, dtype=np.int8)
+    N, K = b.shape
+    if K % TERN_GROUP:
+        raise ValueError("tern_pack_b1: K % 128 != 0")
+    bits = np.empty((N, K // 32), dtype=np.uint32)
+    _check(_lib.tern_pack_b1(_np_ptr(b), N, K, _np_ptr(bits)), "tern_pack_b1")
+    return bits
+
+
+def tern_unpack_b1(bits: np.ndarray, K: int) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    N = bits.shape[0]
+    b = np.empty((N, K), dtype=np.int8)
+    _check(_lib.tern_unpack_b1(_np_ptr(bits), N, K, _np_ptr(b)), "tern_unpack_b1")
+    return b
+
+
+def tern_b1_to_codes(bits: np.ndarray, K: int) -> np.ndarray:
+    """Binary bit words [N, K/32] -> ternary slot codes [N, K/16] (t = b)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    N = bits.shape[0]
+    if bits.shape != (N, K // 32):
+        raise ValueError("tern_b1_to_codes: bits must be [N, K/32]")
+    codes = np.empty((N, K // 16), dtype=np.uint32)
+    _check(_lib.tern_b1_to_codes(_np_ptr(bits), N, K, _np_ptr(codes)), "tern_b1_to_codes")
+    return codes
+
+
+def tern_codes_to_b1(codes: np.ndarray, K: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    N = codes.shape[0]
+    if codes.shape != (N, K // 16):
+        raise ValueError("tern_codes_to_b1: codes must be [N, K/16]")
+    bits = np.empty((N, K // 32), dtype=np.uint32)
+    _check(_lib.tern_codes_to_b1(_np_ptr(codes), N, K, _np_ptr(bits)), "tern_codes_to_b1")
+    return bits
 
 
 # --------------------------------------------------------------------------

@@ -290,4 +290,315 @@ tern_status tern_dequant_f32(const uint32_t *codes, const uint16_t *s_f16, int64
     return TERN_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Format variants ("prism-ml/Ternary-Bonsai-27B-mlx-2bit" model card,
+// sections "Shipped components", "MLX packaging", and the 1-bit row of the
+// variant table under "Benchmarks").
+// ---------------------------------------------------------------------------
+
+size_t tern_scales_g64_bytes(int64_t N, int64_t K)
+{
+    if (!sizes_ok(N, K)) return 0;
+    return (size_t)N * (size_t)(K / 64) * 2u;
+}
+
+size_t tern_b1_bytes(int64_t N, int64_t K)
+{
+    if (!sizes_ok(N, K)) return 0;
+    return (size_t)N * (size_t)(K / 32) * 4u;
+}
+
+tern_status tern_scales_to_g64(const uint16_t *s, int64_t N, int64_t K, uint16_t *s64)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_scales_to_g64: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!s || !s64) {
+        set_error("tern_scales_to_g64: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    // back to front, so that s64 may start at s (in-place widening)
+    for (int64_t i = G - 1; i >= 0; --i) {
+        const uint16_t h = s[i];
+        s64[2 * i + 1] = h;
+        s64[2 * i] = h;
+    }
+    return TERN_OK;
+}
+
+tern_status tern_scales_from_g64(const uint16_t *s64, int64_t N, int64_t K, uint16_t *s)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_scales_from_g64: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!s64 || !s) {
+        set_error("tern_scales_from_g64: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    for (int64_t i = 0; i < G; ++i) {
+        const uint16_t a = s64[2 * i], b = s64[2 * i + 1];
+        if (!half_finite(a) || !half_finite(b)) {
+            set_error("tern_scales_from_g64: non-finite scale in group " + std::to_string(i));
+            return TERN_EINVAL;
+        }
+        if (half_bits_to_float(a) != half_bits_to_float(b)) {
+            set_error("tern_scales_from_g64: the two 64-blocks of group " + std::to_string(i) +
+                      " have different scales");
+            return TERN_ENOTTERNARY;
+        }
+    }
+    for (int64_t i = 0; i < G; ++i) s[i] = s64[2 * i];  // forward: s may start at s64
+    return TERN_OK;
+}
+
+tern_status tern_mlx_export(const uint16_t *s, int64_t N, int64_t K, uint16_t *mlx_scales,
+                            uint16_t *mlx_biases)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_mlx_export: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!s || !mlx_scales || !mlx_biases) {
+        set_error("tern_mlx_export: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    for (int64_t i = 0; i < G; ++i)
+        if (!half_finite(s[i])) {
+            set_error("tern_mlx_export: non-finite scale at index " + std::to_string(i));
+            return TERN_EINVAL;
+        }
+    for (int64_t i = 0; i < G; ++i) {
+        const uint16_t h = s[i];
+        mlx_biases[i] = (uint16_t)(h ^ 0x8000u);  // -s: a sign flip, exact
+        mlx_scales[i] = h;
+    }
+    return TERN_OK;
+}
+
+tern_status tern_mlx_import(const uint16_t *mlx_scales, const uint16_t *mlx_biases, int64_t N, int64_t K,
+                            uint16_t *s)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_mlx_import: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!mlx_scales || !mlx_biases || !s) {
+        set_error("tern_mlx_import: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    for (int64_t i = 0; i < G; ++i) {
+        const uint16_t a = mlx_scales[i], b = mlx_biases[i];
+        if (!half_finite(a) || !half_finite(b)) {
+            set_error("tern_mlx_import: non-finite scale or bias in group " + std::to_string(i));
+            return TERN_EINVAL;
+        }
+        if (half_bits_to_float(b) != -half_bits_to_float(a)) {
+            set_error("tern_mlx_import: group " + std::to_string(i) +
+                      " has bias != -scale (not a ternary group on slots q = t + 1)");
+            return TERN_ENOTTERNARY;
+        }
+    }
+    if (s != mlx_scales) std::memmove(s, mlx_scales, (size_t)G * 2u);
+    return TERN_OK;
+}
+
+tern_status tern_pack_b1(const int8_t *b, int64_t N, int64_t K, uint32_t *bits)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_pack_b1: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!b || !bits) {
+        set_error("tern_pack_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t W = K / 32;
+    std::vector<char> bad(N, 0);
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1; ++n)
+            for (int64_t w = 0; w < W; ++w) {
+                uint32_t word = 0;
+                for (int j = 0; j < 32; ++j) {
+                    const int v = b[n * K + 32 * w + j];
+                    if (v != 1 && v != -1) bad[n] = 1;
+                    word |= (uint32_t)(v == 1) << j;
+                }
+                bits[n * W + w] = word;
+            }
+    });
+    for (int64_t n = 0; n < N; ++n)
+        if (bad[n]) {
+            set_error("tern_pack_b1: value other than -1 or +1 in row " + std::to_string(n));
+            return TERN_ENOTTERNARY;
+        }
+    return TERN_OK;
+}
+
+tern_status tern_unpack_b1(const uint32_t *bits, int64_t N, int64_t K, int8_t *b)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_unpack_b1: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!bits || !b) {
+        set_error("tern_unpack_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t W = K / 32;
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t i = r0 * W; i < r1 * W; ++i)
+            for (int j = 0; j < 32; ++j) b[32 * i + j] = ((bits[i] >> j) & 1u) ? (int8_t)1 : (int8_t)-1;
+    });
+    return TERN_OK;
+}
+
+namespace {
+// Bits 0..15 of v moved to the even positions 0, 2, ..., 30.
+uint32_t spread_even(uint32_t v)
+{
+    v &= 0xffffu;
+    v = (v | (v << 8)) & 0x00ff00ffu;
+    v = (v | (v << 4)) & 0x0f0f0f0fu;
+    v = (v | (v << 2)) & 0x33333333u;
+    v = (v | (v << 1)) & 0x55555555u;
+    return v;
+}
+}  // namespace
+
+tern_status tern_b1_to_codes(const uint32_t *bits, int64_t N, int64_t K, uint32_t *codes)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_b1_to_codes: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!bits || !codes) {
+        set_error("tern_b1_to_codes: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t W = K / 32;
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t i = r0 * W; i < r1 * W; ++i) {
+            // bit 1 (+1) -> slot 2, bit 0 (-1) -> slot 0: q = 2 * bit
+            codes[2 * i] = spread_even(bits[i]) << 1;
+            codes[2 * i + 1] = spread_even(bits[i] >> 16) << 1;
+        }
+    });
+    return TERN_OK;
+}
+
+tern_status tern_codes_to_b1(const uint32_t *codes, int64_t N, int64_t K, uint32_t *bits)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_codes_to_b1: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!codes || !bits) {
+        set_error("tern_codes_to_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t W = K / 32;
+    std::vector<char> bad(N, 0);  // 1: a zero weight, 2: slot value 3
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1; ++n)
+            for (int64_t w = 0; w < W; ++w) {
+                uint32_t word = 0;
+                for (int j = 0; j < 32; ++j) {
+                    const uint32_t c = codes[n * 2 * W + 2 * w + (j >> 4)];
+                    const uint32_t q = (c >> (2 * (j & 15))) & 3u;
+                    if (q == 3) bad[n] = 2;
+                    else if (q == 1 && !bad[n]) bad[n] = 1;
+                    word |= (uint32_t)(q == 2) << j;
+                }
+                bits[n * W + w] = word;
+            }
+    });
+    for (int64_t n = 0; n < N; ++n) {
+        if (bad[n] == 2) {
+            set_error("tern_codes_to_b1: slot value 3 in row " + std::to_string(n));
+            return TERN_EBADCODE;
+        }
+        if (bad[n] == 1) {
+            set_error("tern_codes_to_b1: zero weight (no binary code) in row " + std::to_string(n));
+            return TERN_ENOTTERNARY;
+        }
+    }
+    return TERN_OK;
+}
+
+tern_status tern_mlx_export_b1(const uint16_t *s, int64_t N, int64_t K, uint16_t *mlx_scales,
+                               uint16_t *mlx_biases)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_mlx_export_b1: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!s || !mlx_scales || !mlx_biases) {
+        set_error("tern_mlx_export_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    for (int64_t i = 0; i < G; ++i) {
+        const uint32_t e = (s[i] >> 10) & 0x1fu;
+        if (e >= 30) {  // non-finite, or 2s does not fit binary16
+            set_error("tern_mlx_export_b1: scale at index " + std::to_string(i) +
+                      (e == 31 ? " is not finite" : " overflows binary16 when doubled"));
+            return TERN_EINVAL;
+        }
+    }
+    for (int64_t i = 0; i < G; ++i) {
+        const uint16_t h = s[i];
+        const uint32_t sign = h & 0x8000u, mag = h & 0x7fffu;
+        // 2s exactly: one more in the exponent for a normal number; for a
+        // subnormal the fraction doubles (and may carry into the exponent)
+        const uint32_t twice = ((mag >> 10) == 0) ? (mag << 1) : (mag + 0x400u);
+        mlx_biases[i] = (uint16_t)(h ^ 0x8000u);
+        mlx_scales[i] = (uint16_t)(sign | twice);
+    }
+    return TERN_OK;
+}
+
+tern_status tern_mlx_import_b1(const uint16_t *mlx_scales, const uint16_t *mlx_biases, int64_t N, int64_t K,
+                               uint16_t *s)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_mlx_import_b1: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!mlx_scales || !mlx_biases || !s) {
+        set_error("tern_mlx_import_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = N * (K / kGroup);
+    for (int64_t i = 0; i < G; ++i) {
+        const uint16_t a = mlx_scales[i], b = mlx_biases[i];
+        if (!half_finite(a) || !half_finite(b)) {
+            set_error("tern_mlx_import_b1: non-finite scale or bias in group " + std::to_string(i));
+            return TERN_EINVAL;
+        }
+        if (half_bits_to_float(a) != -2.0f * half_bits_to_float(b)) {
+            set_error("tern_mlx_import_b1: group " + std::to_string(i) + " has scale != -2 * bias");
+            return TERN_ENOTTERNARY;
+        }
+    }
+    for (int64_t i = 0; i < G; ++i) s[i] = (uint16_t)(mlx_biases[i] ^ 0x8000u);
+    return TERN_OK;
+}
+
 }  // extern "C"

@@ -587,3 +587,43 @@ def test_rotation_fold_into_weight_rows(tern, b):
     y_ref = x.astype(np.float64) @ W.astype(np.float64).T
     scale = np.abs(x).astype(np.float64) @ np.abs(W).astype(np.float64).T
     assert np.all(np.abs(y_fold - y_ref) <= 1e-5 * scale)
+
+
+# ---------------------------------------------------------------------------
+# format variants: converted on the host, run through the g128 kernels, and
+# checked against the oracle's dense weights of the variant itself
+# ---------------------------------------------------------------------------
+
+def _variant_problem(tern, oracle_lib, fmt, N, K, seed):
+    """Returns (codes, g128 scales) for the kernels and the oracle's dense
+    float64 weights of the variant as given."""
+    s = synth.scales_f16(seed, N, K)
+    if fmt == "b1":
+        b = np.where(np.random.default_rng(seed).random((N, K)) < 0.5, 1, -1).astype(np.int8)
+        bits = tern.tern_pack_b1(b)
+        dense = oracle_lib.b1_decode(bits, K) * np.repeat(oracle_lib.half_bits_to_f64(s), 128, axis=1)
+        return tern.tern_b1_to_codes(bits, K), s, dense
+    t = synth.ternary(seed, N, K, 0.35)
+    codes, _ = tern.tern_pack(t, s)
+    if fmt == "g64":
+        s64 = np.repeat(s, 2, axis=1)
+        return codes, tern.tern_scales_from_g64(s64), oracle_lib.dequant_g64(codes, s64, K)
+    sc, bi = np.ascontiguousarray(s), s | np.uint16(0x8000)      # (s, -s)
+    return codes, tern.tern_mlx_import(sc, bi), oracle_lib.dequant_affine(codes, 2, 128, sc, bi, K)
+
+
+@pytest.mark.parametrize("fmt", ["b1", "g64", "mlx"])
+@pytest.mark.parametrize("M,K,N,op", [(1, 1024, 300, "gemv"), (5, 2304, 129, "gemv"), (96, 1280, 200, "gemm")])
+def test_format_variant_through_kernels(tern, oracle_lib, fmt, M, K, N, op):
+    seed = 800 + M + K + N
+    print(f"variant {fmt} {op} M={M} K={K} N={N} seed={seed}", flush=True)
+    codes, s, dense = _variant_problem(tern, oracle_lib, fmt, N, K, seed)
+    x = synth.activations_bf16(seed, M, K)
+    codes_d, scales_d = tern.to_device(codes, s)
+    fn = tern.tern_gemv if op == "gemv" else tern.tern_gemm
+    y = fn(x_to_device(x), codes_d, scales_d)
+    torch().cuda.synchronize()
+    xd = oracle_lib.bf16_bits_to_f64(x)
+    y_ref = xd @ dense.T
+    bound = np.abs(xd) @ np.abs(dense).T
+    assert_matmul_close(y_to_host(y), y_ref, bound, what=f"{fmt} {op} M{M} K{K} N{N}")
