@@ -70,6 +70,10 @@ def lib():
         L.oracle_b1_encode.argtypes = [P, I64, I64, P]
         L.oracle_format_bits_per_weight.argtypes = [ctypes.c_int, I64, I64]
         L.oracle_format_bits_per_weight.restype = ctypes.c_double
+        L.oracle_t5_decode.argtypes = [P, I64, I64, P]
+        L.oracle_t5_encode.argtypes = [P, I64, I64, P]
+        L.oracle_t5_bits_per_weight.argtypes = [I64, I64]
+        L.oracle_t5_bits_per_weight.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -288,3 +292,36 @@ def b1_encode(b: np.ndarray) -> np.ndarray:
     if lib().oracle_b1_encode(_ptr(b), N, K, _ptr(bits)):
         raise ValueError("not binary")
     return bits
+
+
+# ---------------------------------------------------------------------------
+# base-3 layout: five ternary values per byte, groups taken five at a time
+# ---------------------------------------------------------------------------
+
+def t5_row_bytes(K: int) -> int:
+    return ((K // 128 + 4) // 5) * 128
+
+
+def t5_encode(t: np.ndarray) -> np.ndarray:
+    """int8 t [N, K] in {-1,0,1} -> uint8 [N, ceil(K/640) * 128]."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    N, K = t.shape
+    assert K % 128 == 0
+    d = np.zeros((N, t5_row_bytes(K)), dtype=np.uint8)
+    if lib().oracle_t5_encode(_ptr(t), N, K, _ptr(d)):
+        raise ValueError("not ternary")
+    return d
+
+
+def t5_decode(d: np.ndarray, K: int) -> np.ndarray:
+    d = np.ascontiguousarray(d, dtype=np.uint8)
+    N = d.shape[0]
+    assert d.shape == (N, t5_row_bytes(K))
+    t = np.zeros((N, K), dtype=np.int8)
+    if lib().oracle_t5_decode(_ptr(d), N, K, _ptr(t)):
+        raise ValueError("byte out of range for its superblock")
+    return t
+
+
+def t5_bits_per_weight(N: int, K: int) -> float:
+    return lib().oracle_t5_bits_per_weight(N, K)

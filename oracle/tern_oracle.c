@@ -341,3 +341,66 @@ double oracle_format_bits_per_weight(int format, int64_t N, int64_t K)
     }
     return 8.0 * (field_bytes + side_bytes) / nk;
 }
+
+/* ------------------------------------------------------------------------
+ * Base-3 layout below two bits per weight.  The card ("Memory requirement")
+ * notes that 2-bit slots cost 2.125 bits/weight against about 1.71 for the
+ * information content, and that native ternary kernels would close the gap;
+ * it does not give a layout.  This one packs five ternary values into a byte
+ * (3^5 = 243 <= 256), 1.6 bits per weight:
+ *   - the groups of 128 of a row are taken five at a time ("superblocks");
+ *     superblock b holds groups 5b .. 5b + p - 1, p = min(5, G - 5b);
+ *   - superblock b is 128 bytes; byte i holds sum_{j<p} q_j 3^j with q_j = t + 1
+ *     of weight k = 128 (5b + j) + i, i.e. digit j of byte i is weight i of
+ *     the superblock's group j;
+ *   - a row is ceil(G/5) * 128 bytes; scales stay one FP16 per group.
+ * --------------------------------------------------------------------- */
+
+static int64_t t5_row_bytes(int64_t K)
+{
+    int64_t G = K / ORACLE_GROUP;
+    return ((G + 4) / 5) * 128;
+}
+
+/* Decode into t.  Returns 0, or 3 if a byte is not below 3^p. */
+int oracle_t5_decode(const uint8_t *d, int64_t N, int64_t K, int8_t *t)
+{
+    const int64_t G = K / ORACLE_GROUP, rb = t5_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t g = k / ORACLE_GROUP, b = g / 5, j = g % 5;
+            int64_t p = (G - 5 * b) < 5 ? (G - 5 * b) : 5;
+            int v = d[n * rb + 128 * b + k % ORACLE_GROUP];
+            int lim = 1;
+            for (int e = 0; e < p; ++e) lim *= 3;
+            if (v >= lim) return 3;
+            for (int e = 0; e < j; ++e) v /= 3;
+            t[n * K + k] = (int8_t)(v % 3 - 1);
+        }
+    return 0;
+}
+
+/* Encode t in {-1,0,+1}.  Returns 0, or 2 if some t is not ternary.  d must
+ * hold N * ceil(K/640) * 128 bytes. */
+int oracle_t5_encode(const int8_t *t, int64_t N, int64_t K, uint8_t *d)
+{
+    const int64_t rb = t5_row_bytes(K);
+    for (int64_t i = 0; i < N * rb; ++i) d[i] = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int v = t[n * K + k];
+            if (v < -1 || v > 1) return 2;
+            int64_t g = k / ORACLE_GROUP, b = g / 5, j = g % 5;
+            int w = 1;
+            for (int e = 0; e < j; ++e) w *= 3;
+            d[n * rb + 128 * b + k % ORACLE_GROUP] += (uint8_t)((v + 1) * w);
+        }
+    return 0;
+}
+
+/* Bits per weight of the base-3 layout with its FP16 group scales. */
+double oracle_t5_bits_per_weight(int64_t N, int64_t K)
+{
+    double bytes = (double)N * (double)t5_row_bytes(K) + 2.0 * (double)N * (double)(K / ORACLE_GROUP);
+    return 8.0 * bytes / ((double)N * (double)K);
+}

@@ -510,3 +510,64 @@ def test_b1_encode_rejects_non_binary(oracle_lib):
         b[1, 77] = bad
         with pytest.raises(ValueError):
             oracle_lib.b1_encode(b)
+
+
+# ---------------------------------------------------------------------------
+# base-3 layout (five ternary values per byte, superblocks of five groups)
+# ---------------------------------------------------------------------------
+
+def _np_t5(t):
+    """The base-3 layout built with numpy reshapes: digit j of byte i of
+    superblock b is weight i of group 5b + j; missing groups are zero digits."""
+    N, K = t.shape
+    G = K // 128
+    SB = (G + 4) // 5
+    q = np.zeros((N, SB * 5, 128), dtype=np.int64)
+    q[:, :G, :] = (t.astype(np.int64) + 1).reshape(N, G, 128)
+    q = q.reshape(N, SB, 5, 128)
+    w = (3 ** np.arange(5, dtype=np.int64))[None, None, :, None]
+    return (q * w).sum(axis=2).reshape(N, SB * 128).astype(np.uint8)
+
+
+def test_t5_every_byte_value(oracle_lib):
+    v = np.arange(243, dtype=np.uint8)
+    d = np.repeat(v[:, None], 128, axis=1)             # K = 640: one full superblock
+    t = oracle_lib.t5_decode(d, 640)
+    for j in range(5):
+        digit = (v.astype(np.int64) // 3 ** j) % 3
+        assert np.array_equal(t[:, 128 * j:128 * (j + 1)], np.repeat(digit[:, None] - 1, 128, axis=1))
+    assert np.array_equal(oracle_lib.t5_encode(t), d)
+    for bad in (243, 255):
+        e = d[:1].copy()
+        e[0, 77] = bad
+        with pytest.raises(ValueError):
+            oracle_lib.t5_decode(e, 640)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 7, 13, 40, 136])
+def test_t5_layout_matches_numpy(oracle_lib, G):
+    K = 128 * G
+    t = synth.ternary(900 + G, 5, K)
+    d = oracle_lib.t5_encode(t)
+    assert d.shape == (5, ((G + 4) // 5) * 128)
+    assert np.array_equal(d, _np_t5(t))
+    assert np.array_equal(oracle_lib.t5_decode(d, K), t)
+    p = G % 5
+    if p:                                              # the tail superblock holds p digits
+        e = d.copy()
+        e[2, -1] = 3 ** p
+        with pytest.raises(ValueError):
+            oracle_lib.t5_decode(e, K)
+        e[2, -1] = 3 ** p - 1
+        assert oracle_lib.t5_decode(e, K)[2, -1] == 1
+
+
+def test_t5_accounting(oracle_lib):
+    g = _golden()
+    for N, K in [(1, 640), (17408, 5120), (248320, 5120)]:
+        assert oracle_lib.t5_bits_per_weight(N, K) == 1.6 + 16 / 128
+    info = math.log2(3) + 16 / 128
+    assert round(info, 2) == g["effective_bits_per_weight"]
+    assert info < oracle_lib.t5_bits_per_weight(1, 640) < g["deployed_bits_per_weight"]
+    # a ragged tail costs a whole superblock: K = 4096 is 7 superblocks for 32 groups
+    assert oracle_lib.t5_bits_per_weight(1, 4096) == 8 * (7 * 128 + 64) / 4096
