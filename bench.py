@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="rotated",
-                   choices=["rotated", "sweep", "prefill", "chain", "copy", "all"],
+                   choices=["rotated", "sweep", "prefill", "chain", "base3", "copy", "all"],
                    help="rotated: the headline step; sweep / prefill: extra measurements; "
                         "copy: a plain device copy of known size (counter calibration)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -264,6 +264,55 @@ def bench_sweep(tern, torch, synth, steps):
     return out
 
 
+def t5_gemv_bytes(M, K, N):
+    """Algorithmic bytes of a GEMV over the base-3 layout: ceil(K/640) * 128
+    bytes per row, FP16 scales, bf16 activations, fp32 output."""
+    return N * ((K // 128 + 4) // 5) * 128 + 2 * N * K // 128 + M * K * 2 + M * N * 4
+
+
+def bench_t5(tern, torch, synth, steps):
+    """Decode GEMV over the base-3 layout (1.6 bits/weight) beside the 2-bit
+    GEMV on the same weights, M = 1 and 16, rotated pools, graph-timed."""
+    out = {}
+    for (K, N) in ((4096, 12288), (5120, 17408), (17408, 5120)):
+        seed = 7 + K
+        t = synth.ternary(seed, N, K)
+        s = synth.scales_f16(seed, N, K)
+        codes, s2 = tern.tern_pack(t, s)
+        data = tern.tern_pack_t5(codes, K)
+        d0 = torch.from_numpy(data).cuda()
+        s0 = torch.from_numpy(s2.view(np.int16)).cuda()
+        copies = max(2, -(-POOL_BYTES // (data.size + s2.nbytes)))
+        pool = [(d0, s0)] + [(d0.clone(), s0.clone()) for _ in range(copies - 1)]
+        pool2 = make_pool(tern, torch, t, s, tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K))
+        for M in (1, 16):
+            x = synth.activations_bf16(seed, M, K)
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+            def fn(i, xd=xd, y=y):
+                d, s_ = pool[i % len(pool)]
+                tern.tern_gemv_t5(xd, d, s_, out=y)
+
+            def fn2(i, xd=xd, y=y):
+                c, s_ = pool2[i % len(pool2)]
+                tern.tern_gemv(xd, c, s_, out=y)
+
+            for i in range(5):
+                fn(i)
+                fn2(i)
+            ms, _ = time_graph(torch, fn, steps)
+            ms2, _ = time_graph(torch, fn2, steps)
+            us, us2 = 1e3 * ms / steps, 1e3 * ms2 / steps
+            gbs = t5_gemv_bytes(M, K, N) / (us * 1e-6) / 1e9
+            out[f"M{M}_K{K}_N{N}"] = {"us": us, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                      "bytes": t5_gemv_bytes(M, K, N), "us_2bit": us2,
+                                      "bytes_2bit": gemv_bytes(M, K, N, 2)}
+        del pool, pool2, d0, s0
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill(tern, torch, synth, steps):
     out = {}
     for w in synth.PREFILL:
@@ -364,6 +413,9 @@ def main():
     if args.workload == "chain":
         print(json.dumps({"chain": bench_chain(tern, torch, synth)}))
         return
+    if args.workload == "base3":
+        print(json.dumps({"base3": bench_t5(tern, torch, synth, args.steps)}))
+        return
 
     w, host, res = bench_rotated(args, tern, torch, synth)
     line = {
@@ -391,6 +443,7 @@ def main():
             "decode_sweep_gemv": bench_sweep(tern, torch, synth, 200),
             "prefill_gemm": bench_prefill(tern, torch, synth, 20),
             "decode_pass_27b_class": bench_chain(tern, torch, synth),
+            "decode_gemv_base3": bench_t5(tern, torch, synth, 200),
         }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, host)

@@ -195,6 +195,27 @@ tern_status tern_mlx_import_b1(const uint16_t *mlx_scales, const uint16_t *mlx_b
                                int64_t N, int64_t K, uint16_t *s);
 
 /* ---------------------------------------------------------------------------
+ * Base-3 layout below two bits per weight.  "Memory requirement" notes that
+ * 2-bit slots cost 2.125 bits/weight against about 1.71 for the information
+ * content, to be closed by native ternary kernels; the layout is not given,
+ * and this one is ours: five ternary values per byte (3^5 = 243 <= 256).
+ * The groups of 128 of a row are taken five at a time; superblock b (128
+ * bytes) holds groups 5b .. 5b + p - 1, p = min(5, K/128 - 5b), and its byte i
+ * holds sum_{j<p} (t + 1) 3^j over weights k = 128 (5b + j) + i.  A row is
+ * ceil(K/640) * 128 bytes (1.6 bits/weight when K is a multiple of 640); the
+ * binary16 scales [N][K/128] are unchanged.  data: uint8 [N][ceil(K/640)*128].
+ * ------------------------------------------------------------------------ */
+size_t tern_t5_bytes(int64_t N, int64_t K);
+
+/* 2-bit slot codes [N][K/16] -> base-3 data.  TERN_EBADCODE for slot value 3
+ * (data then undefined); TERN_EINVAL for sizes or NULL.  Host pointers. */
+tern_status tern_pack_t5(const uint32_t *codes, int64_t N, int64_t K, uint8_t *data);
+
+/* Base-3 data -> 2-bit slot codes.  TERN_EBADCODE if a byte is not below
+ * 3^p for its superblock (codes then undefined); TERN_EINVAL.  Host pointers. */
+tern_status tern_unpack_t5(const uint8_t *data, int64_t N, int64_t K, uint32_t *codes);
+
+/* ---------------------------------------------------------------------------
  * Device operations.  Device pointers; enqueued on `stream`.
  * ------------------------------------------------------------------------ */
 
@@ -234,6 +255,16 @@ tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, in
 tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K,
                       const uint32_t *codes, const uint16_t *scales, int64_t N,
                       void *y, int ydt, void *stream);
+
+/* tern_gemv over the base-3 layout: the same product and accuracy, with the
+ * weights streamed at 1.6 bits/weight (plus scales) and their digits decoded
+ * in the kernel.  x: [M][K] TERN_BF16 only, 16-byte aligned; data as above,
+ * 16-byte aligned; scales [N][K/128]; y [M][N] as ydt.  Bytes out of range for
+ * their superblock give unspecified results (tern_unpack_t5 checks them).
+ * Errors: TERN_EINVAL (M > 16, sizes, alignment, NULL), TERN_EUNSUPPORTED
+ * (TERN_F32 activations, dtype), TERN_EDEVICE. */
+tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uint8_t *data,
+                         const uint16_t *scales, int64_t N, void *y, int ydt, void *stream);
 
 /* Rotated decode in one launch: y = (H_b D x / sqrt(b)) (s_g t)^T, i.e. the
  * signed normalized Walsh-Hadamard transform of tern_fwht (forward, blocks

@@ -30,9 +30,10 @@ EXPORTED = [
     "tern_gemm", "tern_scales_g64_bytes", "tern_scales_to_g64", "tern_scales_from_g64",
     "tern_mlx_export", "tern_mlx_import", "tern_b1_bytes", "tern_pack_b1", "tern_unpack_b1",
     "tern_b1_to_codes", "tern_codes_to_b1", "tern_mlx_export_b1", "tern_mlx_import_b1",
+    "tern_t5_bytes", "tern_pack_t5", "tern_unpack_t5", "tern_gemv_t5",
 ]
 _SIZE_FNS = ("tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes",
-             "tern_scales_g64_bytes", "tern_b1_bytes")
+             "tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libtern.so is not built ({LIB_PATH}); run __graft_entry__.build()")
@@ -62,11 +63,12 @@ _lib.tern_rotate_gemv.argtypes = [_P, _I, _P, _I64, _I64, _I64, _P, _P, _I64, _P
 _lib.tern_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 _lib.tern_gemm_workspace_bytes.restype = _SZ
 _lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
-for _name in ("tern_scales_g64_bytes", "tern_b1_bytes"):
+_lib.tern_gemv_t5.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
+for _name in ("tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes"):
     getattr(_lib, _name).argtypes = [_I64, _I64]
     getattr(_lib, _name).restype = _SZ
 for _name in ("tern_scales_to_g64", "tern_scales_from_g64", "tern_pack_b1", "tern_unpack_b1",
-              "tern_b1_to_codes", "tern_codes_to_b1"):
+              "tern_b1_to_codes", "tern_codes_to_b1", "tern_pack_t5", "tern_unpack_t5"):
     getattr(_lib, _name).argtypes = [_P, _I64, _I64, _P]
 for _name in ("tern_mlx_export", "tern_mlx_export_b1"):
     getattr(_lib, _name).argtypes = [_P, _I64, _I64, _P, _P]
@@ -279,6 +281,31 @@ def tern_codes_to_b1(codes: np.ndarray, K: int) -> np.ndarray:
     return bits
 
 
+def tern_t5_bytes(N: int, K: int) -> int:
+    return _lib.tern_t5_bytes(N, K)
+
+
+def tern_pack_t5(codes: np.ndarray, K: int) -> np.ndarray:
+    """2-bit slot codes [N, K/16] -> base-3 data uint8 [N, ceil(K/640) * 128]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    N = codes.shape[0]
+    if K % TERN_GROUP or codes.shape != (N, K // 16):
+        raise ValueError("tern_pack_t5: codes must be [N, K/16] with K % 128 == 0")
+    data = np.empty((N, ((K // TERN_GROUP) + 4) // 5 * 128), dtype=np.uint8)
+    _check(_lib.tern_pack_t5(_np_ptr(codes), N, K, _np_ptr(data)), "tern_pack_t5")
+    return data
+
+
+def tern_unpack_t5(data: np.ndarray, K: int) -> np.ndarray:
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    N = data.shape[0]
+    if K % TERN_GROUP or data.shape != (N, ((K // TERN_GROUP) + 4) // 5 * 128):
+        raise ValueError("tern_unpack_t5: data must be [N, ceil(K/640) * 128]")
+    codes = np.empty((N, K // 16), dtype=np.uint32)
+    _check(_lib.tern_unpack_t5(_np_ptr(data), N, K, _np_ptr(codes)), "tern_unpack_t5")
+    return codes
+
+
 # --------------------------------------------------------------------------
 # device operations (torch tensors on the current HIP device)
 # --------------------------------------------------------------------------
@@ -362,6 +389,19 @@ def tern_rotate_gemv(x, signs, block: int, codes, scales, out=None, out_dtype=No
     _check(_lib.tern_rotate_gemv(_dev_ptr(x), _dt(x), _dev_ptr(signs), block, M, K, _dev_ptr(codes),
                                  _dev_ptr(scales), N, _dev_ptr(out), _dt(out), _stream_ptr(stream)),
            "tern_rotate_gemv")
+    return out
+
+
+def tern_gemv_t5(x, data, scales, out=None, out_dtype=None, stream=None):
+    """y [M, N] = x [M, K] (bfloat16, M <= 16) times the base-3 weights (data
+    uint8 [N, ceil(K/640) * 128] on the device) with their group scales."""
+    T = _torch()
+    M, K = x.shape
+    N = data.shape[0]
+    if out is None:
+        out = T.empty((M, N), dtype=out_dtype or T.float32, device=x.device)
+    _check(_lib.tern_gemv_t5(_dev_ptr(x), _dt(x), M, K, _dev_ptr(data), _dev_ptr(scales), N,
+                             _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv_t5")
     return out
 
 

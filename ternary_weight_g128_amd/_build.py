@@ -16,6 +16,7 @@ LIB = os.path.join(HERE, "libtern.so")
 SOURCES = [
     ("tern_kernels.hip", []),
     ("tern_gemm.hip", ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]),
+    ("tern_t5.hip", []),
     ("tern_api.cpp", []),
     ("tern_codec.cpp", []),
 ]

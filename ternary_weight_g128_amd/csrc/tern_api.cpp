@@ -171,6 +171,48 @@ tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32
         "tern_gemm");
 }
 
+tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uint8_t *data,
+                         const uint16_t *scales, int64_t N, void *y, int ydt, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) {
+        set_error("tern_gemv_t5: negative size");
+        return TERN_EINVAL;
+    }
+    if (K % TERN_GROUP != 0) {
+        set_error("tern_gemv_t5: K must be a multiple of 128 (whole scale groups)");
+        return TERN_EINVAL;
+    }
+    if (M > TERN_GEMV_MAX_M) {
+        set_error("tern_gemv_t5: M must be at most 16");
+        return TERN_EINVAL;
+    }
+    if (xdt != TERN_BF16) {
+        set_error("tern_gemv_t5: activations must be TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (ydt != TERN_F32 && ydt != TERN_BF16) {
+        set_error("tern_gemv_t5: output dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (!y || (K > 0 && (!x || !data || !scales))) {
+        set_error("tern_gemv_t5: NULL pointer");
+        return TERN_EINVAL;
+    }
+    if (!aligned(y, ydt == TERN_F32 ? 4 : 2) ||
+        (K > 0 && (!aligned(x, 16) || !aligned(data, 16) || !aligned(scales, 2)))) {
+        set_error("tern_gemv_t5: x and data must be 16-byte aligned, scales 2-byte, y to its dtype");
+        return TERN_EINVAL;
+    }
+    if (N > ((int64_t)1 << 31) - 64 || K > ((int64_t)1 << 24) ||
+        N * tern::t5_row_bytes(K) >= ((int64_t)1 << 40)) {
+        set_error("tern_gemv_t5: matrix too large");
+        return TERN_EINVAL;
+    }
+    return device_status(tern::launch_gemv_t5(x, (int)M, K, data, scales, N, y, ydt == TERN_BF16, stream),
+                         "tern_gemv_t5");
+}
+
 tern_status tern_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream)
 {
     if (N < 0 || K < 0) {

@@ -601,4 +601,90 @@ tern_status tern_mlx_import_b1(const uint16_t *mlx_scales, const uint16_t *mlx_b
     return TERN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Base-3 layout: five ternary values per byte (see tern.h)
+// ---------------------------------------------------------------------------
+
+size_t tern_t5_bytes(int64_t N, int64_t K)
+{
+    if (!sizes_ok(N, K)) return 0;
+    return (size_t)N * (size_t)(((K / kGroup) + 4) / 5) * 128u;
+}
+
+tern_status tern_pack_t5(const uint32_t *codes, int64_t N, int64_t K, uint8_t *data)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_pack_t5: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!codes || !data) {
+        set_error("tern_pack_t5: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = K / kGroup, SB = (G + 4) / 5, W = K / kSlots;
+    std::vector<char> bad(N, 0);
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1; ++n)
+            for (int64_t b = 0; b < SB; ++b) {
+                const int64_t p = std::min<int64_t>(5, G - 5 * b);
+                for (int i = 0; i < 128; ++i) {
+                    unsigned v = 0, w3 = 1;
+                    for (int64_t j = 0; j < p; ++j, w3 *= 3) {
+                        const int64_t k = 128 * (5 * b + j) + i;
+                        const unsigned q = (codes[n * W + k / kSlots] >> (2 * (k % kSlots))) & 3u;
+                        if (q == 3) bad[n] = 1;
+                        v += (q == 3 ? 0u : q) * w3;
+                    }
+                    data[(n * SB + b) * 128 + i] = (uint8_t)v;
+                }
+            }
+    });
+    for (int64_t n = 0; n < N; ++n)
+        if (bad[n]) {
+            set_error("tern_pack_t5: slot value 3 in row " + std::to_string(n));
+            return TERN_EBADCODE;
+        }
+    return TERN_OK;
+}
+
+tern_status tern_unpack_t5(const uint8_t *data, int64_t N, int64_t K, uint32_t *codes)
+{
+    if (!sizes_ok(N, K)) {
+        set_error("tern_unpack_t5: need N >= 0, K >= 0 and K % 128 == 0");
+        return TERN_EINVAL;
+    }
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!data || !codes) {
+        set_error("tern_unpack_t5: NULL pointer");
+        return TERN_EINVAL;
+    }
+    const int64_t G = K / kGroup, SB = (G + 4) / 5, W = K / kSlots;
+    std::vector<char> bad(N, 0);
+    for_rows(N, K, [&](int64_t r0, int64_t r1) {
+        for (int64_t n = r0; n < r1; ++n) {
+            for (int64_t w = 0; w < W; ++w) codes[n * W + w] = 0;
+            for (int64_t b = 0; b < SB; ++b) {
+                const int64_t p = std::min<int64_t>(5, G - 5 * b);
+                unsigned lim = 1;
+                for (int64_t j = 0; j < p; ++j) lim *= 3;
+                for (int i = 0; i < 128; ++i) {
+                    unsigned v = data[(n * SB + b) * 128 + i];
+                    if (v >= lim) { bad[n] = 1; v = 0; }
+                    for (int64_t j = 0; j < p; ++j, v /= 3) {
+                        const int64_t k = 128 * (5 * b + j) + i;
+                        codes[n * W + k / kSlots] |= (v % 3) << (2 * (k % kSlots));
+                    }
+                }
+            }
+        }
+    });
+    for (int64_t n = 0; n < N; ++n)
+        if (bad[n]) {
+            set_error("tern_unpack_t5: byte outside the range of its superblock in row " + std::to_string(n));
+            return TERN_EBADCODE;
+        }
+    return TERN_OK;
+}
+
 }  // extern "C"

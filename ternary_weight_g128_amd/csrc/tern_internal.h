@@ -31,6 +31,9 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes,
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int launch_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream);
 int64_t gemm_max_k();
+int launch_gemv_t5(const void *x, int M, int64_t K, const uint8_t *data, const uint16_t *scales, int64_t N,
+                   void *y, bool y_bf16, void *stream);
+int64_t t5_row_bytes(int64_t K);
 
 const char *hip_error_string(int err);
 

@@ -191,3 +191,44 @@ def test_b1_affine_export_every_scale(tern, oracle_lib):
     with pytest.raises(tern.TernError) as e:
         tern.tern_mlx_import_b1(bad, bi)
     assert e.value.status == tern.TERN_ENOTTERNARY
+
+
+# ---------------------------------------------------------------------------
+# base-3 layout (five ternary values per byte)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 128), (9, 512), (17, 640), (33, 4096), (64, 5120), (40, 17408)])
+def test_t5_pack_matches_oracle(tern, oracle_lib, N, K):
+    t = synth.ternary(960 + N + K, N, K, 0.35)
+    codes = oracle_lib.encode(t)
+    data = tern.tern_pack_t5(codes, K)
+    assert np.array_equal(data, oracle_lib.t5_encode(t))
+    assert np.array_equal(tern.tern_unpack_t5(data, K), codes)
+    assert tern.tern_t5_bytes(N, K) == data.size
+    bpw = 8 * (data.size + tern.tern_scales_bytes(N, K)) / (N * K)
+    assert bpw == oracle_lib.t5_bits_per_weight(N, K)
+
+
+def test_t5_every_byte_and_tail_width(tern, oracle_lib):
+    for G in (1, 2, 3, 4, 5):
+        K = 128 * G
+        lim = 3 ** G
+        d = np.zeros((lim, 128), dtype=np.uint8)
+        d[:, :] = np.arange(lim, dtype=np.int64)[:, None]
+        codes = tern.tern_unpack_t5(d, K)
+        assert np.array_equal(tern.tern_unpack(codes, K), oracle_lib.t5_decode(d, K))
+        assert np.array_equal(tern.tern_pack_t5(codes, K), d)
+        if lim < 256:
+            bad = d[:1].copy()
+            bad[0, 100] = lim
+            with pytest.raises(tern.TernError) as e:
+                tern.tern_unpack_t5(bad, K)
+            assert e.value.status == tern.TERN_EBADCODE
+
+
+def test_t5_pack_rejects_slot_three(tern):
+    codes = np.zeros((2, 640 // 16), dtype=np.uint32)
+    codes[1, 9] = 3 << 6
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_pack_t5(codes, 640)
+    assert e.value.status == tern.TERN_EBADCODE

@@ -627,3 +627,107 @@ def test_format_variant_through_kernels(tern, oracle_lib, fmt, M, K, N, op):
     y_ref = xd @ dense.T
     bound = np.abs(xd) @ np.abs(dense).T
     assert_matmul_close(y_to_host(y), y_ref, bound, what=f"{fmt} {op} M{M} K{K} N{N}")
+
+
+# ---------------------------------------------------------------------------
+# decode GEMV over the base-3 layout (five ternary values per byte)
+# ---------------------------------------------------------------------------
+
+T5_SHAPES = [
+    # (M, K, N): one to five groups in the last superblock, ragged tiles, M up to 16
+    (1, 128, 1), (1, 256, 17), (2, 384, 33), (1, 512, 64), (3, 640, 100), (1, 768, 31),
+    (4, 1280, 257), (5, 4096, 48), (8, 5120, 40), (16, 2304, 300), (1, 6144, 129),
+    (7, 17408, 20), (16, 17408, 35),
+]
+
+
+def _run_t5(tern, x, data, s, ydt="f32"):
+    """data: the base-3 bytes as the oracle's encoder writes them."""
+    T = torch()
+    out_dtype = T.float32 if ydt == "f32" else T.bfloat16
+    y = tern.tern_gemv_t5(x_to_device(x), T.from_numpy(data).cuda(),
+                          T.from_numpy(s.view(np.int16)).cuda(), out_dtype=out_dtype)
+    T.cuda.synchronize()
+    return y_to_host(y)
+
+
+@pytest.mark.parametrize("M,K,N", T5_SHAPES)
+def test_gemv_t5_matches_oracle(tern, oracle_lib, M, K, N):
+    seed = 31 * M + K + 7 * N
+    print(f"gemv_t5 M={M} K={K} N={N} seed={seed}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K)
+    y = _run_t5(tern, x, oracle_lib.t5_encode(t), s)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y, y_ref, bound, what=f"gemv_t5 M{M} K{K} N{N}")
+
+
+def test_gemv_t5_integer_exact_and_bf16_out(tern, oracle_lib):
+    """Integer activations and scales in {0.5, 1, 2}: every partial sum is
+    exact in binary32, so the result is bit-exact; bf16 output rounds once."""
+    N, K, M = 70, 3200, 3
+    rng = np.random.default_rng(4242)
+    t = synth.ternary(4242, N, K)
+    s = rng.choice(np.array([0x3800, 0x3C00, 0x4000], dtype=np.uint16), size=(N, K // 128))
+    xi = rng.integers(-64, 65, size=(M, K)).astype(np.float32)
+    x = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    data = oracle_lib.t5_encode(t)
+    y = _run_t5(tern, x, data, s)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert np.array_equal(y, y_ref)
+    yb = _run_t5(tern, x, data, s, "bf16")
+    assert_matmul_close(yb, y_ref, bound, bf16_out=True, what="gemv_t5 bf16 out")
+
+
+def test_gemv_t5_every_byte_value(tern, oracle_lib):
+    """Rows whose bytes run through all 243 values (every digit pattern at
+    every group position), integer activations: bit-exact."""
+    K = 640 * 2 + 256                                  # two full superblocks and a two-group tail
+    G = K // 128
+    N = 243
+    v = np.arange(243, dtype=np.int64)
+    t = np.zeros((N, K), dtype=np.int8)
+    for g in range(G):
+        j = g % 5
+        # roll the row index per position so that every byte holds many values
+        idx = (v[:, None] + np.arange(128)[None, :] * 7 + g) % 243
+        t[:, 128 * g:128 * (g + 1)] = ((idx // 3 ** j) % 3 - 1).astype(np.int8)
+    s = np.full((N, G), 0x3C00, dtype=np.uint16)
+    rng = np.random.default_rng(243)
+    xi = rng.integers(-64, 65, size=(2, K)).astype(np.float32)
+    x = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    data = oracle_lib.t5_encode(t)
+    assert len(np.unique(data[:, :256])) == 243
+    y = _run_t5(tern, x, data, s)
+    y_ref, _ = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert np.array_equal(y, y_ref)
+
+
+def test_gemv_t5_zero_and_empty(tern, oracle_lib):
+    T = torch()
+    K, N = 1280, 40
+    t = np.zeros((N, K), dtype=np.int8)
+    s = synth.scales_f16(5, N, K)
+    x = synth.activations_bf16(5, 2, K)
+    assert np.all(_run_t5(tern, x, oracle_lib.t5_encode(t), s) == 0)
+    xk0 = T.zeros((2, 0), dtype=T.bfloat16, device="cuda")
+    y = tern.tern_gemv_t5(xk0, T.zeros((N, 0), dtype=T.uint8, device="cuda"),
+                          T.zeros((N, 0), dtype=T.int16, device="cuda"))
+    T.cuda.synchronize()
+    assert y.shape == (2, N) and bool((y == 0).all())
+
+
+@pytest.mark.parametrize("K,N", [(5120, 17408), (17408, 5120), (4096, 12288)])
+def test_gemv_t5_full_size_sampled(tern, oracle_lib, K, N):
+    """Full decode shapes in the launch configuration the benchmark times;
+    sampled rows checked against the oracle."""
+    T = torch()
+    print(f"gemv_t5 full K={K} N={N}", flush=True)
+    rows = sampled_rows(N, 40, K + N)
+    t = synth.ternary(K + 3 * N, N, K, 0.35)
+    s = synth.scales_f16(K + 3 * N, N, K)
+    x = synth.activations_bf16(K, 1, K)
+    y = _run_t5(tern, x, oracle_lib.t5_encode(t), s)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t[rows]), s[rows], K)
+    assert_matmul_close(y[:, rows], y_ref, bound, what=f"gemv_t5 full K{K} N{N}")
