@@ -96,36 +96,6 @@ struct GemmArgs {
     int64_t items;          // r * s leftover pieces
 };
 
-// Weight operands without per-pair shifts.  For a code word w, plane s
-// (s = 0..3) is ((w ^ 0x55555555) << (6 - 2 s)) & m: byte b of it holds the
-// flipped slot 4 b + s at bits 7..6 and zeros elsewhere (m = 0xC0C0C0C0, or
-// 0 for a zero-scale group).  A bfloat16 pair of the MFMA operand -- slots
-// 2p and 2p + 1 at bits 15..14 and 31..30 -- is then one byte permute of
-// two planes: byte p >> 1 of plane 2 (p & 1) into byte 1, the same byte of
-// plane 2 (p & 1) + 1 into byte 3, zeros elsewhere.
-constexpr unsigned kPlaneMask = 0xC0C0C0C0u;
-
-__device__ __forceinline__ void code_planes(unsigned w, unsigned m, unsigned (&t)[4])
-{
-    t[0] = ((w << 6) ^ (kFlip << 6)) & m;
-    t[1] = ((w << 4) ^ (kFlip << 4)) & m;
-    t[2] = ((w << 2) ^ (kFlip << 2)) & m;
-    t[3] = (w ^ kFlip) & m;
-}
-
-// MFMA B operand for slots 8h .. 8h + 7 of a word (element e = slot 8h + e).
-__device__ __forceinline__ bf16x8_t operand_from_planes(const unsigned (&t)[4], int h)
-{
-    u32x4_t p;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int pair = 4 * h + v, b = pair >> 1;
-        const unsigned sel = 0x0Cu | ((unsigned)b << 8) | (0x0Cu << 16) | ((4u + b) << 24);
-        p[v] = (pair & 1) ? __builtin_amdgcn_perm(t[3], t[2], sel) : __builtin_amdgcn_perm(t[1], t[0], sel);
-    }
-    return __builtin_bit_cast(bf16x8_t, p);
-}
-
 // Position in the tile of accumulator element e in MFMA register order
 // e = ((((wave * MI + i) * 2 + j) * 16 + v) * 64 + lane): lane (c, g) of
 // sub-tile (i, j) holds row 32 i + 8 (v >> 2) + 4 g + (v & 3), column

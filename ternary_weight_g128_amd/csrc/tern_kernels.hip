@@ -32,6 +32,7 @@ namespace {
 #include "tern_device.h"
 
 
+
 // Hadamard helpers (natural Sylvester order: a butterfly over every index
 // bit).  See the transform section below for the data layout.
 // Element index for thread t (within a block) and register index r when the
@@ -214,10 +215,17 @@ __device__ __forceinline__ uint32_t quad_scale(uint32_t sq, int j)
 // butterflies there (same register-radix-16 passes as the stand-alone
 // transform, while the code stream is already in flight), scales by
 // 1/sqrt(b) and stages the result as hi/lo bfloat16 rows (XF32 == true).
-template <int MX, bool XF32, int TPW, bool SC4, int ROT = 0, int ROTL = 0>
+// AG: the A operand comes straight from global memory instead of an LDS
+// image of x (bfloat16 input, no rotation): lane (row i, lane group g) reads
+// the eight consecutive activations k = 128 G + 32 {0, 2, 1, 3}[g] + 8 mu +
+// 0..7 of MFMA mu of scale group G, and the weight operand is built in the
+// same consecutive order from byte planes of the raw code word.  Nothing of x
+// is staged, so LDS does not limit the workgroups per CU for larger M.
+template <int MX, bool XF32, int TPW, bool SC4, int ROT = 0, int ROTL = 0, bool AG = false>
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 {
     static_assert(ROT == 0 || XF32, "rotated activations are staged as hi/lo rows");
+    static_assert(!AG || (!XF32 && ROT == 0), "direct A loads take bfloat16 activations");
     constexpr int PF = 4;
     constexpr int kDist = 2;
     constexpr bool kQuadScales = MX <= 4;
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     // compiler can count outstanding loads exactly.
     __bf16 *lds_x = reinterpret_cast<__bf16 *>(smem);
     const int rowpad = a.K + (a.K >> 4);  // padded row of the rotation scratch
-    float *rot = reinterpret_cast<float *>(smem + (size_t)a.K * MX * 2);
+    float *rot = reinterpret_cast<float *>(smem + (AG ? 0 : (size_t)a.K * MX * 2));
     float *red = rot + (ROT ? (size_t)a.M * rowpad : 0);
 
     // 1. activation loads for the first staging batch go out first, so that
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     XUnit<XF32> xu[kUB];
     u32x4_t du[kUB];  // signs of the unit (rotation)
 #pragma unroll
-    for (int i = 0; i < kUB; ++i) {
+    for (int i = 0; i < (AG ? 0 : kUB); ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
         load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
@@ -355,12 +363,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
         }
     };
 #pragma unroll
-    for (int i = 0; i < kUB; ++i) {
+    for (int i = 0; i < (AG ? 0 : kUB); ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
         put(xu[i], du[i], u);
     }
-    for (int u0 = kUB * nthreads; u0 < units; u0 += kUB * nthreads) {
+    for (int u0 = kUB * nthreads; u0 < (AG ? 0 : units); u0 += kUB * nthreads) {
 #pragma unroll
         for (int i = 0; i < kUB; ++i) {
             int u = u0 + threadIdx.x + i * nthreads;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             put(xu[i], du[i], u);
         }
     }
-    __syncthreads();
+    if constexpr (!AG) __syncthreads();
     if constexpr (ROT != 0) {
         // Hadamard butterflies over each block of 2^log2b along K, four
         // index bits per pass; a group is 16 values that differ only in the
@@ -442,6 +450,24 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     const __bf16 *lds_lane = lds_x + (g * MX + arow) * 8;
     constexpr int kGroupStride = 16 * MX * 8;  // bf16 elements per staged group
     constexpr int kMuStride = 4 * MX * 8;
+    // AG: A operands of the two groups of a block, loaded one block ahead
+    bf16x8_t ag[2][8];
+    const bf16x8_t zero8 = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    const __bf16 *xrow = static_cast<const __bf16 *>(a.x) + (int64_t)arow * a.K +
+                         32 * (((g & 1) << 1) | (g >> 1));
+    auto load_a = [&](int b, int slot) {
+        if constexpr (AG) {
+            b = b < nblocks ? b : nblocks - 1;
+            const int gl0 = g_begin + 2 * b;
+            const int gl1 = (gl0 + 1 < g_end) ? gl0 + 1 : gl0;
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) {
+                ag[slot][mu] = a_active ? *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu) : zero8;
+                ag[slot][4 + mu] = a_active ? *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu) : zero8;
+            }
+        }
+    };
+    if constexpr (AG) load_a(0, 0);
 
     // One block: A operands from LDS, consume ring slot p (regroup and flip
     // the code words into fresh registers), refill the slot, then two
@@ -450,7 +476,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     auto process = [&](int b, int p, const uint32_t (&sq)[TPW], bool refill) {
         const int gl0 = g_begin + 2 * b;
         const bool two = gl0 + 1 < g_end;
-        if (a_active) {
+        if constexpr (AG) {
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) {
+                a0[mu] = ag[p & 1][mu];
+                a1[mu] = ag[p & 1][4 + mu];
+            }
+            load_a(b + 1, (p + 1) & 1);
+        } else if (a_active) {
             const __bf16 *pa0 = lds_lane + gl0 * kGroupStride;
             const __bf16 *pa1 = pa0 + (two ? kGroupStride : 0);
 #pragma unroll
@@ -465,10 +498,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
         for (int tp = 0; tp < TPW; ++tp) {
             auto s02 = __builtin_amdgcn_permlane32_swap(cbuf[p][tp][0], cbuf[p][tp][2], false, false);
             auto s13 = __builtin_amdgcn_permlane32_swap(cbuf[p][tp][1], cbuf[p][tp][3], false, false);
-            wq[tp][0] = s02[0] ^ kFlip;  // group 0, operand half 0
-            wq[tp][1] = s13[0] ^ kFlip;  // group 0, operand half 1
-            wq[tp][2] = s02[1] ^ kFlip;  // group 1, operand half 0
-            wq[tp][3] = s13[1] ^ kFlip;  // group 1, operand half 1
+            const unsigned flip = AG ? 0u : kFlip;  // the planes apply the flip themselves
+            wq[tp][0] = s02[0] ^ flip;  // group 0, operand half 0
+            wq[tp][1] = s13[0] ^ flip;  // group 0, operand half 1
+            wq[tp][2] = s02[1] ^ flip;  // group 1, operand half 0
+            wq[tp][3] = s13[1] ^ flip;  // group 1, operand half 1
             const uint32_t pair = kQuadScales ? quad_scale(sq[tp], p) : sbuf[p][tp];
             sc[tp][0] = half_to_float((uint16_t)(pair & 0xffffu));
             sc[tp][1] = two ? half_to_float((uint16_t)(pair >> 16)) : 0.0f;
@@ -480,14 +514,32 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             acc0[tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             acc1[tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        if constexpr (AG) {
+            unsigned pl[TPW][4][4];
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu) {
+            for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
-            for (int tp = 0; tp < TPW; ++tp) {
-                acc0[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a0[mu], weights_operand(wq[tp][mu >> 1], mu & 1), acc0[tp], 0, 0, 0);
-                acc1[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a1[mu], weights_operand(wq[tp][2 + (mu >> 1)], mu & 1), acc1[tp], 0, 0, 0);
+                for (int w = 0; w < 4; ++w) code_planes(wq[tp][w], kPlaneMask, pl[tp][w]);
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) {
+#pragma unroll
+                for (int tp = 0; tp < TPW; ++tp) {
+                    acc0[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a0[mu], operand_from_planes(pl[tp][mu >> 1], mu & 1), acc0[tp], 0, 0, 0);
+                    acc1[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a1[mu], operand_from_planes(pl[tp][2 + (mu >> 1)], mu & 1), acc1[tp], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) {
+#pragma unroll
+                for (int tp = 0; tp < TPW; ++tp) {
+                    acc0[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a0[mu], weights_operand(wq[tp][mu >> 1], mu & 1), acc0[tp], 0, 0, 0);
+                    acc1[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a1[mu], weights_operand(wq[tp][2 + (mu >> 1)], mu & 1), acc1[tp], 0, 0, 0);
+                }
             }
         }
 #pragma unroll
@@ -699,6 +751,7 @@ struct GemvPlan {
     int tpw, wk, wt;
     int64_t wgs;
     size_t lds;
+    bool ag;  // A operand straight from global memory (no staged x)
 };
 
 // Tiles per wave and the split of a workgroup's four waves between tiles
@@ -719,14 +772,38 @@ inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
     pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
     const int waves = pl.wt * pl.wk;
     pl.lds = (size_t)K * mx * 2 + (size_t)waves * pl.tpw * mx * kTileN * sizeof(float);
+    pl.ag = false;
+    return pl;
+}
+
+// bfloat16 activations with eight or more A rows (or a staged image too large
+// for LDS): direct A loads, so LDS does not cap the workgroups per CU.  Two
+// tiles per wave and four K-waves, from a sweep of the decode shapes (four
+// tiles per wave spill registers).
+inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx)
+{
+    const int64_t tiles = (N + kTileN - 1) / kTileN;
+    const int nblk = (int)((K / kGroup + 1) / 2);
+    GemvPlan pl;
+    pl.tpw = 2;
+    const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
+    pl.wt = 1;
+    pl.wk = 4;
+    while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
+    pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
+    pl.lds = (size_t)pl.wt * pl.wk * pl.tpw * mx * kTileN * sizeof(float);
+    pl.ag = true;
     return pl;
 }
 
 template <int MX, bool XF32, int TPW>
 int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
-    auto kernel = (a.K / kGroup) % 2 == 0 ? gemv_kernel<MX, XF32, TPW, true>
-                                          : gemv_kernel<MX, XF32, TPW, false>;
+    const bool sc4 = (a.K / kGroup) % 2 == 0;
+    void (*kernel)(GemvArgs) = sc4 ? gemv_kernel<MX, XF32, TPW, true> : gemv_kernel<MX, XF32, TPW, false>;
+    if constexpr (!XF32)
+        if (pl.ag)
+            kernel = sc4 ? gemv_kernel<MX, false, TPW, true, 0, 0, true> : gemv_kernel<MX, false, TPW, false, 0, 0, true>;
     int rc = ensure_lds(kernel, pl.lds);
     if (rc) return rc;
     a.wk = pl.wk;
@@ -740,8 +817,11 @@ int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 template <int MX, bool XF32>
 int launch_gemv_mx(const GemvArgs &a, const GemvPlan &pl, hipStream_t stream)
 {
-    if (pl.tpw == 2) return launch_gemv_t<MX, XF32, 2>(a, pl, stream);
-    return launch_gemv_t<MX, XF32, 1>(a, pl, stream);
+    switch (pl.tpw) {
+    case 1: return launch_gemv_t<MX, XF32, 1>(a, pl, stream);
+    case 2: return launch_gemv_t<MX, XF32, 2>(a, pl, stream);
+    default: return (int)hipErrorInvalidValue;  // plans use one or two tiles per wave
+    }
 }
 
 template <bool XF32>
@@ -749,7 +829,8 @@ int launch_gemv_x(GemvArgs a, hipStream_t stream)
 {
     const int Mx = XF32 ? 2 * a.M : a.M;
     const int mx = Mx <= 1 ? 1 : Mx <= 2 ? 2 : Mx <= 4 ? 4 : Mx <= 8 ? 8 : 16;
-    const GemvPlan pl = plan_gemv(a.N, a.K, mx);
+    GemvPlan pl = plan_gemv(a.N, a.K, mx);
+    if (!XF32 && (mx >= 8 || pl.lds > kMaxLds)) pl = plan_gemv_ag(a.N, a.K, mx);
     switch (mx) {
     case 1: return launch_gemv_mx<1, XF32>(a, pl, stream);
     case 2: return launch_gemv_mx<2, XF32>(a, pl, stream);
@@ -812,7 +893,8 @@ int launch_rotate_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 // several launches over the same weights.
 inline int gemv_rows_per_launch(int64_t N, int64_t K, bool x_f32)
 {
-    const int per = x_f32 ? 2 : 1;
+    if (!x_f32) return 16;  // bfloat16: direct A loads where the staged image would not fit
+    const int per = 2;
     for (int rows = 16 / per; rows > 1; rows /= 2)
         if (plan_gemv(N, K, rows * per).lds <= kMaxLds) return rows;
     return 1;

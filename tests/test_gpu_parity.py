@@ -62,6 +62,36 @@ def test_gemv_matches_oracle(tern, oracle_lib, M, K, N, xdt):
     assert_matmul_close(y, y_ref, bound, what=f"gemv M{M} K{K} N{N} {xdt}")
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 128, 3), (8, 384, 50), (9, 4224, 33), (12, 1152, 257),
+                                   (16, 640, 31), (16, 8448, 100)])
+def test_gemv_direct_activation_loads(tern, oracle_lib, M, K, N):
+    """bfloat16 activations with five or more rows take the direct-A GEMV:
+    one-group tails, odd block counts, ragged tiles."""
+    seed = 77 * M + K + N
+    print(f"gemv direct-A M={M} K={K} N={N} seed={seed}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y, y_ref, bound, what=f"gemv direct-A M{M} K{K} N{N}")
+
+
+def test_gemv_long_k_beyond_lds(tern, oracle_lib):
+    """K so long that the staged activations would not fit in LDS: the
+    bfloat16 GEMV falls back to direct A loads, even for M = 1."""
+    M, K, N = 2, 98304, 24
+    print(f"gemv long K M={M} K={K} N={N}", flush=True)
+    t = synth.ternary(98304, N, K)
+    s = synth.scales_f16(98304, N, K)
+    x = synth.activations_bf16(98304, M, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
+    assert_matmul_close(y, y_ref, bound, what="gemv long K")
+
+
 @pytest.mark.parametrize("M,K,N,xdt", [(1, 1024, 200, "bf16"), (4, 768, 50, "f32"), (16, 256, 20, "bf16")])
 def test_gemv_bf16_output(tern, oracle_lib, M, K, N, xdt):
     seed = 900 + M
