@@ -235,6 +235,36 @@ def cpu_baseline(w, host, min_seconds=10.0):
                       f"naive FP64 matmul over all {w.N} rows), {el:.1f} s, single thread"}
 
 
+def cpu_secondary(synth, seconds=3.0):
+    """The FP64 oracle on bounded samples of the prefill GEMM and the decode
+    GEMV shapes (a slice of output rows over the full K and all M rows of
+    x), single thread; rates are per output computed, so they compare with
+    the GPU figures of the same shapes."""
+    import oracle
+    out = {}
+    cases = [("prefill", w.M, w.K, w.N, w.p_zero, w.outlier_frac) for w in synth.PREFILL] + \
+            [("decode", 1, 5120, 17408, 1 / 3, 0.0), ("decode", 1, 17408, 5120, 1 / 3, 0.0)]
+    for kind, M, K, N, p0, outl in cases:
+        rows = 8 if kind == "prefill" else 64
+        t = synth.ternary(31 + K, rows, K, p0)
+        s = synth.scales_f16(31 + K, rows, K)
+        x = synth.activations_bf16(31 + K, M, K, outl)
+        codes = oracle.encode(t)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.matmul(x, codes, s, K)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        flops = 2.0 * M * rows * K * reps
+        byts = (rows * K // 4 + 2 * rows * K // 128 + M * K * 2 + M * rows * 4) * reps
+        out[f"{kind}_M{M}_K{K}_N{N}"] = {
+            "GFLOP/s": flops / el / 1e9, "GB/s": byts / el / 1e9, "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x ({rows} of {N} output rows, M={M}, full K={K}), {el:.1f} s"}
+    return out
+
+
 def bench_sweep(tern, torch, synth, steps):
     """Decode GEMV at M = 1, 16 on both MLP shapes, rotated pool, graph-timed."""
     out = {}
@@ -447,6 +477,8 @@ def main():
         }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, host)
+        if not args.no_secondary:
+            line["secondary"]["cpu_oracle"] = cpu_secondary(synth)
     print(json.dumps(line))
 
 
