@@ -56,11 +56,15 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    objs = []
-    for src, extra in SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        _run([hipcc(), *HIPCC_FLAGS, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(objdir, src + ".o") for src, _ in SOURCES]
+    # the sources compile independently: one hipcc per source, in parallel
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
+        jobs = [pool.submit(_run, [hipcc(), *HIPCC_FLAGS, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj],
+                            verbose)
+                for (src, extra), obj in zip(SOURCES, objs)]
+        for j in jobs:
+            j.result()
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

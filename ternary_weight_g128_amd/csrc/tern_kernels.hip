@@ -31,6 +31,15 @@ namespace {
 
 #include "tern_device.h"
 
+// Sixteen +1 signs: the sign row read when the caller passes no sign vector,
+// so that the sign load is unconditional (a load under a branch makes the
+// compiler wait for it, and for everything issued before it, at once).
+__device__ const unsigned kOnes16[4] = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+typedef const u32x4_t __attribute__((address_space(1))) gu32x4_t;  // global memory
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef const u32x2_t __attribute__((address_space(1))) gu32x2_t;
+typedef const uint32_t __attribute__((address_space(1))) gu32_t;
+
 
 
 // Hadamard helpers (natural Sylvester order: a butterfly over every index
@@ -120,17 +129,15 @@ template <bool XF32, bool IN_F32 = XF32>
 __device__ __forceinline__ void load_unit(XUnit<XF32> &u, const GemvArgs &a, int m, int wi)
 {
     if constexpr (XF32 && !IN_F32) {
-        // bfloat16 input widened to binary32 words (rotated staging)
+        // bfloat16 input, kept raw in words 0..7 here and widened to binary32
+        // words by widen_unit once it is needed (no arithmetic on loaded
+        // data may sit between the loads and the code stream issued next)
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
             static_cast<const uint16_t *>(a.x) + (int64_t)m * a.K + 16 * wi);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             u32x4_t d = src[q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u.v[8 * q + 2 * e] = d[e] << 16;
-                u.v[8 * q + 2 * e + 1] = d[e] & 0xffff0000u;
-            }
+            u.v[4 * q + 0] = d[0]; u.v[4 * q + 1] = d[1]; u.v[4 * q + 2] = d[2]; u.v[4 * q + 3] = d[3];
         }
     } else if constexpr (XF32) {
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
@@ -148,6 +155,17 @@ __device__ __forceinline__ void load_unit(XUnit<XF32> &u, const GemvArgs &a, int
             u32x4_t d = src[q];
             u.v[4 * q + 0] = d[0]; u.v[4 * q + 1] = d[1]; u.v[4 * q + 2] = d[2]; u.v[4 * q + 3] = d[3];
         }
+    }
+}
+
+// bfloat16 pairs in words 0..7 of a binary32 unit -> binary32 words 0..15.
+__device__ __forceinline__ void widen_unit(XUnit<true> &u)
+{
+#pragma unroll
+    for (int e = 7; e >= 0; --e) {
+        const uint32_t d = u.v[e];
+        u.v[2 * e + 1] = d & 0xffff0000u;
+        u.v[2 * e] = d << 16;
     }
 }
 
@@ -210,11 +228,13 @@ __device__ __forceinline__ uint32_t quad_scale(uint32_t sq, int j)
 // redistributed with cross-row swaps; for larger MX each lane loads its
 // row's pair per block.
 // ROT = 0: x is the activation (binary32 if XF32, else bfloat16).
-// ROT = 1 / 2: x (bfloat16 / binary32) is rotated first: the workgroup
-// computes d .* x in a padded binary32 LDS scratch, applies the Hadamard
-// butterflies there (same register-radix-16 passes as the stand-alone
-// transform, while the code stream is already in flight), scales by
-// 1/sqrt(b) and stages the result as hi/lo bfloat16 rows (XF32 == true).
+// ROT = 1 / 2: x (bfloat16 / binary32) is rotated first, while the code
+// stream is already in flight, and the result is staged as hi/lo bfloat16
+// rows (XF32 == true).  Blocks of 4096 (ROTL == 12): d .* x goes to an LDS
+// scratch as given and the transform H64 X H64 of each block runs on the
+// matrix cores (see kMfmaRot).  Other blocks: d .* x in a padded binary32
+// LDS scratch, the register-radix-16 butterflies of the stand-alone
+// transform there, then 1/sqrt(b).
 // AG: the A operand comes straight from global memory instead of an LDS
 // image of x (bfloat16 input, no rotation): lane (row i, lane group g) reads
 // the eight consecutive activations k = 128 G + 32 {0, 2, 1, 3}[g] + 8 mu +
@@ -227,7 +247,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     static_assert(ROT == 0 || XF32, "rotated activations are staged as hi/lo rows");
     static_assert(!AG || (!XF32 && ROT == 0), "direct A loads take bfloat16 activations");
     constexpr int PF = 4;
-    constexpr int kDist = 2;
+    constexpr int kDist = 2;  // blocks of codes in flight
     constexpr bool kQuadScales = MX <= 4;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int kRowsOut = (MX < 4) ? MX : 4;  // accumulator rows per lane that can be live
@@ -281,17 +301,31 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     const int units = a.M * wpr;
     const int nthreads = 64 * waves;
     constexpr bool kInF32 = ROT ? (ROT == 2) : XF32;
+    // 4096-point blocks go through the matrix cores (rot_unit below); other
+    // blocks use radix-16 butterflies in LDS.
+    constexpr bool kMfmaRot = ROT != 0 && ROTL == 12;
     XUnit<XF32> xu[kUB];
     u32x4_t du[kUB];  // signs of the unit (rotation)
+    const int8_t *sign_src = a.signs ? a.signs : reinterpret_cast<const int8_t *>(kOnes16);
+    auto load_x = [&](int i, int u) {
+        load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
+        if constexpr (ROT != 0)
+            du[i] = *(const gu32x4_t *)(sign_src + (a.signs ? 16 * (u % wpr) : 0));
+    };
+    // matrix-core rotation: d .* x staged once per workgroup in LDS (the
+    // rotation scratch), rows of 64 elements padded to kPadX (conflict-free
+    // 16-byte operand reads)
+    const int rot_per_row = (a.K >> 12) * 4;
+    const int rot_units = a.M * rot_per_row;
+    constexpr int kPadX = ROT == 2 ? 68 : 72;
+    const int xs_row = (a.K >> 6) * kPadX;  // elements per staged row
 #pragma unroll
     for (int i = 0; i < (AG ? 0 : kUB); ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
-        load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
-        if constexpr (ROT != 0)
-            du[i] = a.signs ? *reinterpret_cast<const u32x4_t *>(a.signs + 16 * (u % wpr))
-                            : u32x4_t{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+        load_x(i, u);
     }
+    __builtin_amdgcn_sched_barrier(0);  // activation loads leave first
 
     // 2. code stream: one quad ahead
     const uint32_t *crow[TPW];
@@ -341,10 +375,46 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 #pragma unroll
     for (int p = 0; p < kDist; ++p) load_block(p, p);
     load_quad_scales(0);
+    // Keep the code stream ahead of everything that waits for the
+    // activations: left to itself the scheduler moves the staging arithmetic
+    // (and its wait for x) above these loads, which then leave one full
+    // memory latency late.
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. stage the activations of all of K (shared by the waves)
-    auto put = [&](const XUnit<XF32> &xv, const u32x4_t &dv, int u) {
+    auto put = [&](int i, int u) {
+        XUnit<XF32> &xv = xu[i];
+        const u32x4_t &dv = du[i];
         const int m = u / wpr, wi = u % wpr;
+        if constexpr (kMfmaRot) {
+            // d .* x for the 16 elements k = 16 wi .. 16 wi + 15 (sign bit
+            // flipped where the sign byte is negative), as given: bfloat16
+            // pairs or binary32 words
+            const int k = 16 * wi;
+            if constexpr (ROT == 1) {
+                u32x4_t q[2];
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const uint32_t sel = (v & 1) ? 0x030C020Cu : 0x010C000Cu;  // sign bytes -> bytes 1, 3
+                    q[v >> 2][v & 3] = xv.v[v] ^ (__builtin_amdgcn_perm(0u, dv[v >> 1], sel) & 0x80008000u);
+                }
+                u32x4_t *dst = reinterpret_cast<u32x4_t *>(
+                    reinterpret_cast<uint16_t *>(rot) + (size_t)m * xs_row + (k >> 6) * kPadX + (k & 63));
+                dst[0] = q[0];
+                dst[1] = q[1];
+            } else {
+                u32x4_t q[4];
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    q[e >> 2][e & 3] = xv.v[e] ^ (((dv[e >> 2] >> (8 * (e & 3) + 7)) & 1u) << 31);
+                u32x4_t *dst = reinterpret_cast<u32x4_t *>(
+                    reinterpret_cast<uint32_t *>(rot) + (size_t)m * xs_row + (k >> 6) * kPadX + (k & 63));
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) dst[q4] = q[q4];
+            }
+            return;
+        }
+        if constexpr (XF32 && !kInF32) widen_unit(xv);
         if constexpr (ROT == 0) {
             store_unit<MX, XF32>(lds_x, xv, m, wi);
         } else {
@@ -366,27 +436,156 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     for (int i = 0; i < (AG ? 0 : kUB); ++i) {
         int u = threadIdx.x + i * nthreads;
         u = u < units ? u : units - 1;
-        put(xu[i], du[i], u);
+        put(i, u);
     }
     for (int u0 = kUB * nthreads; u0 < (AG ? 0 : units); u0 += kUB * nthreads) {
 #pragma unroll
         for (int i = 0; i < kUB; ++i) {
             int u = u0 + threadIdx.x + i * nthreads;
             u = u < units ? u : units - 1;
-            load_unit<XF32, kInF32>(xu[i], a, u / wpr, u % wpr);
-            if constexpr (ROT != 0)
-                du[i] = a.signs ? *reinterpret_cast<const u32x4_t *>(a.signs + 16 * (u % wpr))
-                                : u32x4_t{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+            load_x(i, u);
         }
 #pragma unroll
         for (int i = 0; i < kUB; ++i) {
             int u = u0 + threadIdx.x + i * nthreads;
             u = u < units ? u : units - 1;
-            put(xu[i], du[i], u);
+            put(i, u);
         }
     }
     if constexpr (!AG) __syncthreads();
-    if constexpr (ROT != 0) {
+    if constexpr (kMfmaRot) {
+        // A 4096-point block as a 64 x 64 matrix X[i][j] = (d .* x)[64 i + j]:
+        // its transform is H64 X H64 (the Sylvester matrix of 4096 points is
+        // the Kronecker square of the 64-point one).  A unit is one 16-column
+        // slice jt of the result; the wave computes
+        //   Z = X H64[:, 16 jt + 0..15]   (A = rows of X straight from memory)
+        //   X' = H64 Z                    (B = Z as three bfloat16 parts)
+        // on the matrix cores.  The contraction order of the second product
+        // is the order in which the first leaves Z in the lanes (k-slot e of
+        // lane group g at step st is row 32 st + 16 (e >> 2) + 4 g + (e & 3)),
+        // so Z never leaves the registers.  +-1 is exact in bfloat16.
+        const int c = nn;  // this lane's column within a 16-column slice
+        auto pm1 = [](uint32_t lo_neg, uint32_t hi_neg) -> uint32_t {
+            return 0x3F803F80u | ((lo_neg & 1u) << 15) | ((hi_neg & 1u) << 31);
+        };
+        // H64 as the A operand of the second product: row 16 ot + c, k-slot e
+        // as above.  (-1)^popcount of (c & e & 3), ((c >> 2) & g), (ot & 1 &
+        // e >> 2) and (ot >> 1 & st).
+        const uint32_t pl = __builtin_popcount((c >> 2) & g) & 1;
+        const uint32_t q1 = c & 1, q2 = (c >> 1) & 1, q3 = __builtin_popcount(c & 3) & 1;
+        const uint32_t hbase0 = pm1(pl, q1 ^ pl), hbase1 = pm1(q2 ^ pl, q3 ^ pl);
+        bf16x8_t ha[4][2];
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const uint32_t fa = ((ot >> 1) & st) ? 0x80008000u : 0u;  // every slot
+                const uint32_t fb = fa ^ ((ot & 1) ? 0x80008000u : 0u);   // slots e >= 4
+                ha[ot][st] = __builtin_bit_cast(bf16x8_t, u32x4_t{hbase0 ^ fa, hbase1 ^ fa, hbase0 ^ fb, hbase1 ^ fb});
+            }
+        // H64 as the B operand of the first product: column 16 jt + c, k-slot
+        // e -> row 32 ks + 8 g + e.  (-1)^popcount of (e & c & 7), ((g & 1) &
+        // (c >> 3)), ((g >> 1) & jt & 1) and (ks & jt >> 1).
+        const uint32_t pb = (g & 1) & (c >> 3);
+        uint32_t hb0[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            hb0[v] = pm1((__builtin_popcount((2 * v) & c & 7) & 1) ^ pb,
+                         (__builtin_popcount((2 * v + 1) & c & 7) & 1) ^ pb);
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+        auto rot_unit = [&](int u) {
+            const int m = u / rot_per_row, rem = u % rot_per_row, blk = rem >> 2, jt = rem & 3;
+            bf16x8_t hb[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t f = ((((g >> 1) & jt) ^ (ks & (jt >> 1))) & 1) ? 0x80008000u : 0u;
+                hb[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{hb0[0] ^ f, hb0[1] ^ f, hb0[2] ^ f, hb0[3] ^ f});
+            }
+            // Z = (d .* X) H64[:, 16 jt + 0..15]; lane holds Z[16 it + 4 g + r][16 jt + c].
+            // A operand: X[16 it + nn][32 ks + 8 g + 0..7], one staged row segment
+            f32x4_t z[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                z[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int at = m * xs_row + (64 * blk + 16 * it + nn) * kPadX + 32 * ks + 8 * g;
+                    if constexpr (ROT == 1) {
+                        const u32x4_t xa = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(rot) + at);
+                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), hb[ks],
+                                                                        z[it], 0, 0, 0);
+                    } else {
+                        // binary32 input: two bfloat16 parts (16 significand bits)
+                        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint32_t *>(rot) + at);
+                        const u32x4_t w0 = src[0], w1 = src[1];
+                        u32x4_t xh, xl;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float f0 = __builtin_bit_cast(float, v < 2 ? w0[2 * v] : w1[2 * v - 4]);
+                            const float f1 = __builtin_bit_cast(float, v < 2 ? w0[2 * v + 1] : w1[2 * v - 3]);
+                            const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
+                            const bf16x2_t plo = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
+                            xh[v] = __builtin_bit_cast(uint32_t, ph);
+                            xl[v] = __builtin_bit_cast(uint32_t, plo);
+                        }
+                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xh), hb[ks],
+                                                                        z[it], 0, 0, 0);
+                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xl), hb[ks],
+                                                                        z[it], 0, 0, 0);
+                    }
+                }
+            }
+            // Z as three bfloat16 parts: hi + mid + lo carry 24 significand bits
+            u32x4_t zp[3][2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    // k-slots 2v, 2v + 1 of step st: tile 2 st + (v >> 1), rows 2 (v & 1), + 1
+                    float f0 = z[2 * st + (v >> 1)][2 * (v & 1)];
+                    float f1 = z[2 * st + (v >> 1)][2 * (v & 1) + 1];
+#pragma unroll
+                    for (int pt = 0; pt < 3; ++pt) {
+                        const bf16x2_t b = {(__bf16)f0, (__bf16)f1};
+                        zp[pt][st][v] = __builtin_bit_cast(uint32_t, b);
+                        f0 -= (float)b[0];
+                        f1 -= (float)b[1];
+                    }
+                }
+            // X' = H64 Z; lane holds X'[16 ot + 4 g + r][16 jt + c], element
+            // k = 4096 blk + 64 (16 ot + 4 g + r) + 16 jt + c of the row.  Times
+            // 1/64, into the operand image as hi/lo rows 2m, 2m + 1 (the
+            // image position of k is that of store_unit: group k >> 7, word
+            // w = (k >> 4) & 7, slot p = k & 15)
+            const int mu = 2 * (jt & 1) + ((c >> 2) & 1);
+            const int e = 2 * (c & 3) + (c >> 3);
+#pragma unroll
+            for (int ot = 0; ot < 4; ++ot) {
+                f32x4_t o4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int pt = 0; pt < 3; ++pt)
+                        o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[ot][st], __builtin_bit_cast(bf16x8_t, zp[pt][st]),
+                                                                     o4, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ip = 16 * ot + 4 * g + r;
+                    const int G = 32 * blk + (ip >> 1);
+                    const int g2 = 2 * (jt >> 1) + (ip & 1);
+                    const float val = o4[r] * a.norm;
+                    const __bf16 hi = (__bf16)val;
+                    const __bf16 lo = (__bf16)(val - (float)hi);
+                    __bf16 *dst = lds_x + ((((G * 4 + mu) * 4 + g2) * MX + 2 * m) * 8 + e);
+                    dst[0] = hi;
+                    dst[8] = lo;
+                }
+            }
+        };
+        for (int u = wave; u < rot_units; u += waves) rot_unit(u);
+        __syncthreads();
+    } else if constexpr (ROT != 0) {
         // Hadamard butterflies over each block of 2^log2b along K, four
         // index bits per pass; a group is 16 values that differ only in the
         // pass's register bits (see fwht_index).
@@ -843,7 +1042,8 @@ int launch_gemv_x(GemvArgs a, hipStream_t stream)
 
 // Fused rotation: every workgroup transforms the activations once, so use
 // about one workgroup per CU (up to four tiles per wave) and split K over
-// up to four waves (all 256 threads then take part in the butterflies).
+// up to four waves (all of them take part in the transform).  From a sweep
+// of tiles per wave (1..4) x K-waves (1..8) on the rotated decode shape.
 inline GemvPlan plan_rotate_gemv(int64_t N, int64_t K, int M, int mx)
 {
     const int64_t tiles = (N + kTileN - 1) / kTileN;
