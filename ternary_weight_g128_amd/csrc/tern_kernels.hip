@@ -94,7 +94,8 @@ __device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_h
 // (x - hi is exact in binary32; the two parts carry 16 significand bits).
 // The workgroup stages x for all of K in LDS once, permuted so that one
 // 16-byte LDS read gives a lane its A operand for one MFMA; lanes whose A row
-// does not exist never read and keep zeros.  LDS layout in bfloat16
+// does not exist never read and keep zeros (reading for them costs LDS
+// bandwidth: 8x the bytes at M = 1).  LDS layout in bfloat16
 // elements, for scale group G, MFMA index mu = 2 * (operand half) + h, lane
 // group g, A row r and element e: ((((G * 4 + mu) * 4 + g) * MX + r) * 8 + e),
 // where element e of (G, mu, g) holds k = 128 G + 16 w + 4 h + (e >> 1) +
@@ -651,8 +652,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     constexpr int kMuStride = 4 * MX * 8;
     // AG: A operands of the two groups of a block, loaded one block ahead
     bf16x8_t ag[2][8];
-    const bf16x8_t zero8 = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
-    const __bf16 *xrow = static_cast<const __bf16 *>(a.x) + (int64_t)arow * a.K +
+    // lanes whose A row does not exist load row Mx - 1 (always in bounds): their
+    // output rows are never stored, and no select or branch is needed per load
+    const __bf16 *xrow = static_cast<const __bf16 *>(a.x) + (int64_t)(a_active ? arow : Mx - 1) * a.K +
                          32 * (((g & 1) << 1) | (g >> 1));
     auto load_a = [&](int b, int slot) {
         if constexpr (AG) {
@@ -661,8 +663,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             const int gl1 = (gl0 + 1 < g_end) ? gl0 + 1 : gl0;
 #pragma unroll
             for (int mu = 0; mu < 4; ++mu) {
-                ag[slot][mu] = a_active ? *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu) : zero8;
-                ag[slot][4 + mu] = a_active ? *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu) : zero8;
+                ag[slot][mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu);
+                ag[slot][4 + mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu);
             }
         }
     };
@@ -953,11 +955,12 @@ struct GemvPlan {
     bool ag;  // A operand straight from global memory (no staged x)
 };
 
-// Tiles per wave and the split of a workgroup's four waves between tiles
-// (wt) and K (wk), from a sweep of the decode shapes on MI355X: one tile per
-// wave, except two when the staged activations of a workgroup are large
-// (then fewer workgroups stage them); two tile-waves x two K-waves for many
-// tiles, otherwise four K-waves (each with at least two 256-K blocks).
+// Tiles per wave and the split of a workgroup's waves between tiles (wt)
+// and K (wk), from sweeps of the decode shapes on MI355X: one tile per wave,
+// except two when the staged activations of a workgroup are large (then
+// fewer workgroups stage them); two tile-waves x two K-waves for many tiles,
+// otherwise four K-waves, or eight for long rows (each K-wave with at least
+// two 256-K blocks).
 inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
 {
     const int64_t tiles = (N + kTileN - 1) / kTileN;
@@ -967,6 +970,9 @@ inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
     const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
     pl.wt = tile_groups >= 1024 ? 2 : 1;
     pl.wk = 4 / pl.wt;
+    // long rows (32 or more blocks): eight K-waves, each with half the serial
+    // block chain (17408 -> 5120: 12.4 -> 11.5 us at M = 1, 14.7 -> 13.6 at M = 4)
+    if (pl.wt == 1 && nblk >= 32) pl.wk = 8;
     while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
     pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
     const int waves = pl.wt * pl.wk;
