@@ -983,8 +983,8 @@ inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
 
 // bfloat16 activations with eight or more A rows (or a staged image too large
 // for LDS): direct A loads, so LDS does not cap the workgroups per CU.  Two
-// tiles per wave and four K-waves, from a sweep of the decode shapes (four
-// tiles per wave spill registers).
+// tiles per wave (four spill registers) and two K-waves, four for long rows,
+// from sweeps of tiles per wave x tile-waves x K-waves at M = 8 and 16.
 inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx)
 {
     const int64_t tiles = (N + kTileN - 1) / kTileN;
@@ -993,7 +993,7 @@ inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx)
     pl.tpw = 2;
     const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
     pl.wt = 1;
-    pl.wk = 4;
+    pl.wk = nblk >= 32 ? 4 : 2;  // 5120 -> 17408: 21.3 -> 20.5 us at M = 8
     while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
     pl.wgs = (tile_groups + pl.wt - 1) / pl.wt;
     pl.lds = (size_t)pl.wt * pl.wk * pl.tpw * mx * kTileN * sizeof(float);
