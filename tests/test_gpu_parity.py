@@ -45,6 +45,8 @@ GEMV_SHAPES = [
     (1, 128, 1), (1, 128, 17), (1, 384, 33), (1, 1024, 1024), (2, 640, 100),
     (3, 1280, 257), (4, 2048, 31), (5, 896, 48), (8, 768, 64), (9, 384, 40),
     (16, 512, 48), (16, 2304, 300), (1, 4224, 70), (7, 6144, 129),
+    # 32 or more 256-K blocks (eight K-waves), one with a one-group last block
+    (1, 8192, 70), (3, 8320, 33),
 ]
 
 
@@ -305,6 +307,9 @@ def test_rotated_decode_full_size(tern, oracle_lib):
     (1, 4096, 300, 4096, "bf16", True), (1, 4096, 777, 4096, "f32", True), (2, 8192, 100, 4096, "bf16", True),
     (1, 1024, 64, 256, "bf16", False), (3, 2048, 50, 64, "f32", True), (4, 512, 33, 16, "bf16", True),
     (1, 384, 40, 128, "f32", False), (8, 1024, 20, 1024, "bf16", True), (16, 256, 70, 32, "bf16", True),
+    # 4096-point blocks (matrix-core transform): no signs, several units per
+    # wave, staged rows beyond 2M (M = 3 stages 8 rows)
+    (1, 4096, 200, 4096, "bf16", False), (3, 4096, 40, 4096, "f32", False), (4, 4096, 50, 4096, "bf16", True),
 ])
 def test_rotate_gemv_matches_oracle(tern, oracle_lib, M, K, N, block, xdt, signed):
     seed = 3 * M + K + N + block
