@@ -375,7 +375,8 @@ def bench_chain(tern, torch, synth, passes=5):
     lengths match, a link's output (bf16) is the next link's input; the
     6144-wide input of each block's second link is a fixed seeded vector.
     Weights are drawn and packed on the GPU (6.49 GB resident).  `passes`
-    full passes are captured in one HIP graph and timed."""
+    full passes are captured in one HIP graph and timed, and timed again as
+    plain launches on the stream."""
     gen = synth.device_generator(20)
     links = synth.chain_links()
     weights = []
@@ -412,12 +413,24 @@ def bench_chain(tern, torch, synth, passes=5):
     torch.cuda.synchronize()
     ms, _ = time_graph(torch, one_pass, passes)
     ms_pass = ms / passes
+    # the same passes as plain back-to-back launches on the stream (host
+    # launch cost included), HIP events around them
+    cur_stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(cur_stream)
+    for i in range(passes):
+        one_pass(i)
+    end.record(cur_stream)
+    torch.cuda.synchronize()
+    ms_eager = start.elapsed_time(end) / passes
     packed = sum(tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K) for (K, N) in links)
     act = sum(2 * K + (4 if i == len(links) - 1 else 2) * N for i, (K, N) in enumerate(links))
     return {"gemvs": len(links), "packed_bytes": packed, "activation_bytes": act,
             "ms_per_pass": ms_pass, "tokens_per_s": 1e3 / ms_pass,
             "GB/s": (packed + act) / (ms_pass * 1e-3) / 1e9,
-            "frac_hbm": (packed + act) / (ms_pass * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac_hbm": (packed + act) / (ms_pass * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_pass_eager": ms_eager, "tokens_per_s_eager": 1e3 / ms_eager}
 
 
 def main():
