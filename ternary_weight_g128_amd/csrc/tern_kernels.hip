@@ -708,7 +708,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             sc[tp][0] = half_to_float((uint16_t)(pair & 0xffffu));
             sc[tp][1] = two ? half_to_float((uint16_t)(pair >> 16)) : 0.0f;
         }
-        if (refill) load_block(b + kDist, (p + kDist) % PF);
+        // direct A loads: no refill past the last block (M = 16, 5120 -> 17408:
+        // 27.3 -> 25.7 us); the staged path keeps the unconditional clamped
+        // re-load, which lets the compiler count outstanding loads exactly
+        if (refill && (!AG || b + kDist < nblocks)) load_block(b + kDist, (p + kDist) % PF);
         f32x4_t acc0[TPW], acc1[TPW];
 #pragma unroll
         for (int tp = 0; tp < TPW; ++tp) {
