@@ -277,7 +277,10 @@ tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uin
  * (16-byte aligned) or NULL; block: a power of two in [16, 4096] with
  * K % block == 0; M <= 16; codes, scales, y, ydt as tern_gemv.
  * Accuracy: within tern_gemv's bound for the exact rotation plus
- * sum_k |s_g t| |x'_k - exact x'_k| (the rotation is done in binary32).
+ * sum_k |s_g t| |x'_k - exact x'_k| (the rotation is computed to binary32
+ * accuracy: radix-16 butterflies in binary32, or for b = 4096 two bf16
+ * matrix-core products with binary32 accumulation whose binary32 operand is
+ * split exactly into three bfloat16 parts).
  * Errors: as tern_gemv; TERN_EUNSUPPORTED when the staged activations of
  * one workgroup (about 8.25 * M * K bytes) exceed LDS -- use tern_fwht then
  * tern_gemv instead. */
