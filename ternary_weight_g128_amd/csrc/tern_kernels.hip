@@ -69,6 +69,112 @@ __device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_h
     }
 }
 
+// One 16-column slice of a 4096-point transform on the matrix cores.  A
+// block viewed as a 64 x 64 matrix X[i][j] = x[64 i + j] transforms as
+// H64 X H64 (the Sylvester matrix of 4096 points is the Kronecker square of
+// the 64-point one).  The wave computes
+//   Z  = X H64[:, 16 jt + 0..15]   (A = rows of X, B = H64)
+//   X' = H64 Z                     (A = H64, B = Z as three bfloat16 parts)
+// with v_mfma_f32_16x16x32_bf16 and binary32 accumulation.  The contraction
+// order of the second product is the order in which the first leaves Z in
+// the lanes (k-slot e of lane group g at step st is row 32 st + 16 (e >> 2)
+// + 4 g + (e & 3)), so Z never leaves the registers.  +-1 is exact in
+// bfloat16, and hi + mid + lo carry all 24 significand bits of Z.
+// xs: row i of X at element i * (64 + pad) (bfloat16 pairs, or binary32 when
+// IN_F32, which is split into two exact bfloat16 parts for the first
+// product); lane (c = lane & 15, g = lane >> 4); out[ot][r] =
+// X'[16 ot + 4 g + r][16 jt + c], not normalized.
+template <bool IN_F32>
+__device__ __forceinline__ void h64_slice(const void *xs, int jt, int c, int g, f32x4_t (&out)[4])
+{
+    constexpr int kPadX = IN_F32 ? 68 : 72;  // elements per staged row (conflict-free 16-byte reads)
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    auto pm1 = [](uint32_t lo_neg, uint32_t hi_neg) -> uint32_t {
+        return 0x3F803F80u | ((lo_neg & 1u) << 15) | ((hi_neg & 1u) << 31);
+    };
+    // H64 as the A operand of the second product: row 16 ot + c, k-slot e as
+    // above.  (-1)^popcount of (c & e & 3), ((c >> 2) & g), (ot & 1 & e >> 2)
+    // and (ot >> 1 & st).
+    const uint32_t pl = __builtin_popcount((c >> 2) & g) & 1;
+    const uint32_t q1 = c & 1, q2 = (c >> 1) & 1, q3 = __builtin_popcount(c & 3) & 1;
+    const uint32_t hbase0 = pm1(pl, q1 ^ pl), hbase1 = pm1(q2 ^ pl, q3 ^ pl);
+    // H64 as the B operand of the first product: column 16 jt + c, k-slot e
+    // -> row 32 ks + 8 g + e.  (-1)^popcount of (e & c & 7), ((g & 1) &
+    // (c >> 3)), ((g >> 1) & jt & 1) and (ks & jt >> 1).
+    const uint32_t pb = (g & 1) & (c >> 3);
+    bf16x8_t hb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t f = ((((g >> 1) & jt) ^ (ks & (jt >> 1))) & 1) ? 0x80008000u : 0u;
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = pm1((__builtin_popcount((2 * q) & c & 7) & 1) ^ pb,
+                       (__builtin_popcount((2 * q + 1) & c & 7) & 1) ^ pb) ^ f;
+        hb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    // Z; lane holds Z[16 it + 4 g + r][16 jt + c].  A operand: X[16 it + c][32 ks + 8 g + 0..7]
+    f32x4_t z[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        z[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int at = (16 * it + c) * kPadX + 32 * ks + 8 * g;
+            if constexpr (!IN_F32) {
+                const u32x4_t xa = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(xs) + at);
+                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), hb[ks], z[it], 0, 0, 0);
+            } else {
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint32_t *>(xs) + at);
+                const u32x4_t w0 = src[0], w1 = src[1];
+                u32x4_t xh, xl;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float f0 = __builtin_bit_cast(float, v < 2 ? w0[2 * v] : w1[2 * v - 4]);
+                    const float f1 = __builtin_bit_cast(float, v < 2 ? w0[2 * v + 1] : w1[2 * v - 3]);
+                    const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
+                    const bf16x2_t plo = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
+                    xh[v] = __builtin_bit_cast(uint32_t, ph);
+                    xl[v] = __builtin_bit_cast(uint32_t, plo);
+                }
+                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xh), hb[ks], z[it], 0, 0, 0);
+                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xl), hb[ks], z[it], 0, 0, 0);
+            }
+        }
+    }
+    // Z as three bfloat16 parts, in the k-slot order of the second product:
+    // slots 2v, 2v + 1 of step st are tile 2 st + (v >> 1), rows 2 (v & 1), + 1
+    u32x4_t zp[3][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float f0 = z[2 * st + (v >> 1)][2 * (v & 1)];
+            float f1 = z[2 * st + (v >> 1)][2 * (v & 1) + 1];
+#pragma unroll
+            for (int pt = 0; pt < 3; ++pt) {
+                const bf16x2_t b = {(__bf16)f0, (__bf16)f1};
+                zp[pt][st][v] = __builtin_bit_cast(uint32_t, b);
+                f0 -= (float)b[0];
+                f1 -= (float)b[1];
+            }
+        }
+    // X' = H64 Z
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot) {
+        out[ot] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const uint32_t fa = ((ot >> 1) & st) ? 0x80008000u : 0u;  // every slot
+            const uint32_t fb = fa ^ ((ot & 1) ? 0x80008000u : 0u);   // slots e >= 4
+            const bf16x8_t ha = __builtin_bit_cast(bf16x8_t, u32x4_t{hbase0 ^ fa, hbase1 ^ fa, hbase0 ^ fb, hbase1 ^ fb});
+#pragma unroll
+            for (int pt = 0; pt < 3; ++pt)
+                out[ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, __builtin_bit_cast(bf16x8_t, zp[pt][st]), out[ot], 0, 0, 0);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // GEMV for M <= 16
 // ---------------------------------------------------------------------------
@@ -455,134 +561,37 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     }
     if constexpr (!AG) __syncthreads();
     if constexpr (kMfmaRot) {
-        // A 4096-point block as a 64 x 64 matrix X[i][j] = (d .* x)[64 i + j]:
-        // its transform is H64 X H64 (the Sylvester matrix of 4096 points is
-        // the Kronecker square of the 64-point one).  A unit is one 16-column
-        // slice jt of the result; the wave computes
-        //   Z = X H64[:, 16 jt + 0..15]   (A = rows of X straight from memory)
-        //   X' = H64 Z                    (B = Z as three bfloat16 parts)
-        // on the matrix cores.  The contraction order of the second product
-        // is the order in which the first leaves Z in the lanes (k-slot e of
-        // lane group g at step st is row 32 st + 16 (e >> 2) + 4 g + (e & 3)),
-        // so Z never leaves the registers.  +-1 is exact in bfloat16.
-        const int c = nn;  // this lane's column within a 16-column slice
-        auto pm1 = [](uint32_t lo_neg, uint32_t hi_neg) -> uint32_t {
-            return 0x3F803F80u | ((lo_neg & 1u) << 15) | ((hi_neg & 1u) << 31);
-        };
-        // H64 as the A operand of the second product: row 16 ot + c, k-slot e
-        // as above.  (-1)^popcount of (c & e & 3), ((c >> 2) & g), (ot & 1 &
-        // e >> 2) and (ot >> 1 & st).
-        const uint32_t pl = __builtin_popcount((c >> 2) & g) & 1;
-        const uint32_t q1 = c & 1, q2 = (c >> 1) & 1, q3 = __builtin_popcount(c & 3) & 1;
-        const uint32_t hbase0 = pm1(pl, q1 ^ pl), hbase1 = pm1(q2 ^ pl, q3 ^ pl);
-        bf16x8_t ha[4][2];
-#pragma unroll
-        for (int ot = 0; ot < 4; ++ot)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const uint32_t fa = ((ot >> 1) & st) ? 0x80008000u : 0u;  // every slot
-                const uint32_t fb = fa ^ ((ot & 1) ? 0x80008000u : 0u);   // slots e >= 4
-                ha[ot][st] = __builtin_bit_cast(bf16x8_t, u32x4_t{hbase0 ^ fa, hbase1 ^ fa, hbase0 ^ fb, hbase1 ^ fb});
-            }
-        // H64 as the B operand of the first product: column 16 jt + c, k-slot
-        // e -> row 32 ks + 8 g + e.  (-1)^popcount of (e & c & 7), ((g & 1) &
-        // (c >> 3)), ((g >> 1) & jt & 1) and (ks & jt >> 1).
-        const uint32_t pb = (g & 1) & (c >> 3);
-        uint32_t hb0[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            hb0[v] = pm1((__builtin_popcount((2 * v) & c & 7) & 1) ^ pb,
-                         (__builtin_popcount((2 * v + 1) & c & 7) & 1) ^ pb);
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
+        // 4096-point blocks on the matrix cores (h64_slice): a unit is one
+        // 16-column slice jt of one block of one row; the result goes
+        // straight into the operand image, times 1/64, as hi/lo rows 2m and
+        // 2m + 1 (the image position of k is that of store_unit: group
+        // k >> 7, word w = (k >> 4) & 7, slot p = k & 15)
+        const int c = nn;
         auto rot_unit = [&](int u) {
             const int m = u / rot_per_row, rem = u % rot_per_row, blk = rem >> 2, jt = rem & 3;
-            bf16x8_t hb[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint32_t f = ((((g >> 1) & jt) ^ (ks & (jt >> 1))) & 1) ? 0x80008000u : 0u;
-                hb[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{hb0[0] ^ f, hb0[1] ^ f, hb0[2] ^ f, hb0[3] ^ f});
-            }
-            // Z = (d .* X) H64[:, 16 jt + 0..15]; lane holds Z[16 it + 4 g + r][16 jt + c].
-            // A operand: X[16 it + nn][32 ks + 8 g + 0..7], one staged row segment
-            f32x4_t z[4];
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                z[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int at = m * xs_row + (64 * blk + 16 * it + nn) * kPadX + 32 * ks + 8 * g;
-                    if constexpr (ROT == 1) {
-                        const u32x4_t xa = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(rot) + at);
-                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), hb[ks],
-                                                                        z[it], 0, 0, 0);
-                    } else {
-                        // binary32 input: two bfloat16 parts (16 significand bits)
-                        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint32_t *>(rot) + at);
-                        const u32x4_t w0 = src[0], w1 = src[1];
-                        u32x4_t xh, xl;
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float f0 = __builtin_bit_cast(float, v < 2 ? w0[2 * v] : w1[2 * v - 4]);
-                            const float f1 = __builtin_bit_cast(float, v < 2 ? w0[2 * v + 1] : w1[2 * v - 3]);
-                            const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
-                            const bf16x2_t plo = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
-                            xh[v] = __builtin_bit_cast(uint32_t, ph);
-                            xl[v] = __builtin_bit_cast(uint32_t, plo);
-                        }
-                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xh), hb[ks],
-                                                                        z[it], 0, 0, 0);
-                        z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xl), hb[ks],
-                                                                        z[it], 0, 0, 0);
-                    }
-                }
-            }
-            // Z as three bfloat16 parts: hi + mid + lo carry 24 significand bits
-            u32x4_t zp[3][2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    // k-slots 2v, 2v + 1 of step st: tile 2 st + (v >> 1), rows 2 (v & 1), + 1
-                    float f0 = z[2 * st + (v >> 1)][2 * (v & 1)];
-                    float f1 = z[2 * st + (v >> 1)][2 * (v & 1) + 1];
-#pragma unroll
-                    for (int pt = 0; pt < 3; ++pt) {
-                        const bf16x2_t b = {(__bf16)f0, (__bf16)f1};
-                        zp[pt][st][v] = __builtin_bit_cast(uint32_t, b);
-                        f0 -= (float)b[0];
-                        f1 -= (float)b[1];
-                    }
-                }
-            // X' = H64 Z; lane holds X'[16 ot + 4 g + r][16 jt + c], element
-            // k = 4096 blk + 64 (16 ot + 4 g + r) + 16 jt + c of the row.  Times
-            // 1/64, into the operand image as hi/lo rows 2m, 2m + 1 (the
-            // image position of k is that of store_unit: group k >> 7, word
-            // w = (k >> 4) & 7, slot p = k & 15)
+            const size_t at = (size_t)m * xs_row + (size_t)64 * blk * kPadX;
+            const void *xs = ROT == 2 ? (const void *)(reinterpret_cast<const uint32_t *>(rot) + at)
+                                      : (const void *)(reinterpret_cast<const uint16_t *>(rot) + at);
+            f32x4_t o[4];
+            h64_slice<ROT == 2>(xs, jt, c, g, o);
+            // lane holds X'[16 ot + 4 g + r][16 jt + c]: element
+            // k = 4096 blk + 64 (16 ot + 4 g + r) + 16 jt + c of the row
             const int mu = 2 * (jt & 1) + ((c >> 2) & 1);
             const int e = 2 * (c & 3) + (c >> 3);
 #pragma unroll
-            for (int ot = 0; ot < 4; ++ot) {
-                f32x4_t o4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int pt = 0; pt < 3; ++pt)
-                        o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[ot][st], __builtin_bit_cast(bf16x8_t, zp[pt][st]),
-                                                                     o4, 0, 0, 0);
+            for (int ot = 0; ot < 4; ++ot)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int ip = 16 * ot + 4 * g + r;
                     const int G = 32 * blk + (ip >> 1);
                     const int g2 = 2 * (jt >> 1) + (ip & 1);
-                    const float val = o4[r] * a.norm;
+                    const float val = o[ot][r] * a.norm;
                     const __bf16 hi = (__bf16)val;
                     const __bf16 lo = (__bf16)(val - (float)hi);
                     __bf16 *dst = lds_x + ((((G * 4 + mu) * 4 + g2) * MX + 2 * m) * 8 + e);
                     dst[0] = hi;
                     dst[8] = lo;
                 }
-            }
         };
         for (int u = wave; u < rot_units; u += waves) rot_unit(u);
         __syncthreads();
@@ -903,6 +912,69 @@ __global__ __launch_bounds__(256) void fwht16_kernel(
                 y[m * K + sbase + i] = o;
             }
         }
+    }
+}
+
+// Blocks of 4096: one workgroup of four waves per block and row, the block
+// staged once in LDS (d .* x forward, x inverse) and transformed on the
+// matrix cores, one 16-column slice per wave (h64_slice); y = result / 64
+// (times d for the inverse).  Every read of the block precedes the barrier
+// and every write follows it, so y may alias binary32 x.
+template <bool XF32>
+__global__ __launch_bounds__(256) void fwht4096_kernel(const void *__restrict__ x, const int8_t *__restrict__ signs,
+                                                       int64_t M, int64_t K, int inverse, float *y, float norm)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int kPadX = XF32 ? 68 : 72;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 15, g = lane >> 4, t = threadIdx.x;
+    const int64_t k0 = (int64_t)blockIdx.x << 12;  // first element of this block in the row
+    const bool pre = signs && !inverse;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        // thread t stages elements 16 t .. 16 t + 15: row t >> 2 of X, columns 16 (t & 3) ..
+        const int64_t base = m * K + k0 + 16 * t;
+        const u32x4_t dw = pre ? *reinterpret_cast<const u32x4_t *>(signs + k0 + 16 * t)
+                               : u32x4_t{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+        const int at = (t >> 2) * kPadX + 16 * (t & 3);
+        if constexpr (XF32) {
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const float *>(x) + base);
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(reinterpret_cast<uint32_t *>(smem) + at);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4_t v = src[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] ^= ((dw[q] >> (8 * e + 7)) & 1u) << 31;
+                dst[q] = v;
+            }
+        } else {
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(x) + base);
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(smem) + at);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                u32x4_t v = src[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int w = 4 * q + e;  // bfloat16 pair 2w, 2w + 1 of the 16
+                    const uint32_t sel = (w & 1) ? 0x030C020Cu : 0x010C000Cu;  // sign bytes -> bytes 1, 3
+                    v[e] ^= __builtin_amdgcn_perm(0u, dw[w >> 1], sel) & 0x80008000u;
+                }
+                dst[q] = v;
+            }
+        }
+        __syncthreads();
+        f32x4_t o[4];
+        h64_slice<XF32>(smem, wave, c, g, o);
+        // lane holds X'[16 ot + 4 g + r][16 wave + c]: element 64 (16 ot + 4 g + r) + 16 wave + c
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 64 * (16 * ot + 4 * g + r) + 16 * wave + c;
+                float v = o[ot][r] * norm;
+                if (inverse && signs) v *= (float)signs[k0 + i];
+                y[m * K + k0 + i] = v;
+            }
+        __syncthreads();  // the next row's staging reuses the LDS block
     }
 }
 
@@ -1242,6 +1314,16 @@ int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64
     while ((1 << L) < block) ++L;
     const float norm = (float)(1.0 / __builtin_sqrt((double)block));
     const unsigned rows = (unsigned)(M < 65535 ? M : 65535);
+    if (L == 12) {
+        // one workgroup per 4096-point block and row
+        const size_t lds = x_f32 ? 64 * 68 * sizeof(float) : 64 * 72 * sizeof(uint16_t);
+        dim3 grid((unsigned)(K >> 12), rows);
+        if (x_f32)
+            hipLaunchKernelGGL(fwht4096_kernel<true>, grid, dim3(256), lds, st, x, signs, M, K, (int)inverse, y, norm);
+        else
+            hipLaunchKernelGGL(fwht4096_kernel<false>, grid, dim3(256), lds, st, x, signs, M, K, (int)inverse, y, norm);
+        return (int)hipGetLastError();
+    }
     if (L < 4) {
         const int64_t total = M * (K >> L);
         const unsigned grid = (unsigned)((total + 255) / 256 < 65535 * 16 ? (total + 255) / 256 : 65535 * 16);
