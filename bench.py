@@ -38,9 +38,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--reps", type=int, default=7,
+                   help="timed replays of the headline graph (each after a cache flush)")
     p.add_argument("--workload", default="rotated",
-                   choices=["rotated", "sweep", "prefill", "chain", "base3", "copy", "all"],
-                   help="rotated: the headline step; sweep / prefill: extra measurements; "
+                   choices=["rotated", "sweep", "prefill", "chain", "base3", "tiny", "floor", "copy"],
+                   help="rotated: the headline step; sweep / prefill / chain / base3 / tiny: extra "
+                        "measurements; floor: load-only kernels over the decode byte counts; "
                         "copy: a plain device copy of known size (counter calibration)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline line only")
@@ -107,9 +110,29 @@ def make_pool(tern, torch, t, s, nbytes_each):
     return pool
 
 
-def time_graph(torch, fn, steps):
-    """Capture `steps` calls of fn(i) in one HIP graph, replay once, return
-    elapsed ms from HIP events recorded on the replay stream."""
+class Flusher:
+    """Evicts L2 and the 256 MB MALL between timed replays: one read and
+    write of a 1 GiB buffer (a plain torch kernel on the current stream)."""
+
+    def __init__(self, torch, nbytes=1 << 30):
+        self.buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+_FLUSH = None
+
+
+def flusher(torch):
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = Flusher(torch)
+    return _FLUSH
+
+
+def capture(torch, fn, steps):
+    """Capture `steps` calls fn(0) .. fn(steps - 1) in one HIP graph."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -118,17 +141,68 @@ def time_graph(torch, fn, steps):
             for i in range(steps):
                 fn(i)
     torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def time_graph(torch, fn, steps, reps=3):
+    """Capture `steps` calls of fn(i) in one HIP graph and replay it `reps`
+    times, timing each replay with HIP events on the replay stream.  One
+    untimed replay uploads the graph first; before every timed replay the
+    flusher streams 1 GiB through L2 and the MALL, so no timed replay finds
+    the weights it reads in a cache (whatever the step count).  Returns the
+    median replay time in ms, the graph, and median / p10 / p90."""
+    g = capture(torch, fn, steps)
     g.replay()                       # upload / first replay, untimed
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    fl = flusher(torch)
     cur = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        fl()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(cur)
+        g.replay()
+        end.record(cur)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
+    t = np.array(times)
+    stats = {"replays": reps, "steps_per_replay": steps,
+             "median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+             "p90_ms": float(np.percentile(t, 90))}
+    return stats["median_ms"], g, stats
+
+
+def per_step_us(stats):
+    """Median / p10 / p90 of the per-step time (us) over timed replays."""
+    n = stats["steps_per_replay"]
+    return {"median_us": 1e3 * stats["median_ms"] / n, "p10_us": 1e3 * stats["p10_ms"] / n,
+            "p90_us": 1e3 * stats["p90_ms"] / n, "replays": stats["replays"], "steps_per_replay": n}
+
+
+def clocks_under_load(torch, g, replay_ms, seconds=1.5):
+    """GPU clocks read with rocm-smi while the timed graph replays back to
+    back (about `seconds` of queued GPU work), so the clocks are the ones the
+    kernels run at.  Returns the parsed sclk / mclk lines (or the error)."""
+    import subprocess
+    n = int(max(1, seconds * 1e3 / max(replay_ms, 1e-3)))
+    n = min(n, 20000)
+    for _ in range(n):
+        g.replay()
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError) as e:
+        torch.cuda.synchronize()
+        return {"error": str(e)}
     torch.cuda.synchronize()
-    start.record(cur)
-    g.replay()
-    end.record(cur)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end), g
+    res = {}
+    for line in out.splitlines():
+        for key in ("sclk", "mclk", "fclk", "socclk"):
+            if key in line and "(" in line:
+                res[key] = line.split("(")[-1].rstrip(")").strip()
+    res["replays_queued"] = n
+    return res
 
 
 def rotated_step_setup(tern, torch, synth):
@@ -173,16 +247,18 @@ def bench_rotated(args, tern, torch, synth):
         step(i)
     torch.cuda.synchronize()
 
-    # the timed region: exactly `steps` steps, synchronized on both sides
+    # the timed region: exactly `steps` steps per replay, synchronized on
+    # both sides; the median over `reps` replays (each after a cache flush)
     torch.cuda.synchronize()
-    step_ms, g = time_graph(torch, step, args.steps)
+    step_ms, g, stats = time_graph(torch, step, args.steps, reps=args.reps)
     ms_per_step = step_ms / args.steps
-    two_ms, _ = time_graph(torch, two_launch_step, args.steps)
-    gemv_ms, _ = time_graph(torch, gemv_only, args.steps)
-    fwht_ms, _ = time_graph(torch, fwht_only, args.steps)
+    two_ms, _, _ = time_graph(torch, two_launch_step, args.steps)
+    gemv_ms, _, _ = time_graph(torch, gemv_only, args.steps)
+    fwht_ms, _, _ = time_graph(torch, fwht_only, args.steps)
     kernel_us = 1e3 * ms_per_step   # the step is one kernel
     gemv_us = 1e3 * gemv_ms / args.steps
     fwht_us = 1e3 * fwht_ms / args.steps
+    clocks = clocks_under_load(torch, g, step_ms)
 
     # sanity: a replay of the timed graph reproduces the eager result
     step(args.steps - 1)
@@ -204,6 +280,7 @@ def bench_rotated(args, tern, torch, synth):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "detail": {"kernel": "gemv_kernel<2, true, TPW, true, 1> (fused rotation + GEMV)",
                    "kernel_us": kernel_us, "step_bytes": step_bytes,
+                   "step_us_over_replays": per_step_us(stats), "clocks_under_load": clocks,
                    "two_launch_step_us": 1e3 * two_ms / args.steps,
                    "gemv_only_us": gemv_us, "gemv_only_GBps": gemv_bytes(w.M, w.K, w.N, 4) / (gemv_us * 1e-6) / 1e9,
                    "fwht_only_us": fwht_us,
@@ -213,9 +290,24 @@ def bench_rotated(args, tern, torch, synth):
     return w, host, res
 
 
-def cpu_baseline(w, host, min_seconds=10.0):
-    """The FP64 oracle, as it stands, on the same step: explicit-matrix
-    rotation then the naive matmul over all rows, single thread."""
+def host_cpu():
+    """Host CPU model name and the cores this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
+def _time_oracle_steps(w, host, threads, min_seconds):
     import oracle
     t, s, x, d = host
     codes = oracle.encode(t)
@@ -224,44 +316,156 @@ def cpu_baseline(w, host, min_seconds=10.0):
     t0 = time.perf_counter()
     while True:
         xr = oracle.fwht(x64, d, w.rotate_block)
-        oracle.matmul(xr, codes, s, w.K)
+        oracle.matmul(xr, codes, s, w.K, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    step_bytes = rotated_step_bytes(w)
-    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full rotated decode steps (FP64 explicit-Hadamard rotation + "
-                      f"naive FP64 matmul over all {w.N} rows), {el:.1f} s, single thread"}
+    return reps, el
 
 
-def cpu_secondary(synth, seconds=3.0):
-    """The FP64 oracle on bounded samples of the prefill GEMM and the decode
-    GEMV shapes (a slice of output rows over the full K and all M rows of
-    x), single thread; rates are per output computed, so they compare with
-    the GPU figures of the same shapes."""
+def cpu_baseline(w, host, seconds_all=10.0, seconds_one=8.0):
+    """The FP64 oracle, as it stands, on the same step: explicit-matrix
+    rotation, then the naive matmul over all rows.  The reported value uses
+    every host core (the matmul's outputs shared over threads, each output
+    the same k-ordered sum; the small rotation stays on one thread); the
+    single-thread rate of the same program is reported beside it."""
     import oracle
+    model, cores = host_cpu()
+    threads = max(1, min(cores, oracle.max_threads()))
+    step_bytes = rotated_step_bytes(w)
+    reps, el = _time_oracle_steps(w, host, threads, seconds_all)
+    reps1, el1 = _time_oracle_steps(w, host, 1, seconds_one)
+    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cores": cores,
+            "single_core_value": step_bytes * reps1 / el1 / 1e9,
+            "sample": f"{reps} full rotated decode steps in {el:.1f} s on {threads} threads "
+                      f"({reps1} in {el1:.1f} s on 1 thread): FP64 explicit-Hadamard rotation "
+                      f"+ naive FP64 matmul over all {w.N} rows"}
+
+
+def cpu_secondary(synth, seconds=2.0):
+    """The FP64 oracle on bounded samples of the prefill GEMM, the decode GEMV
+    shapes and every link shape of the 27B-class decode pass: a slice of
+    output rows over the full K and all M rows of x, on every host core
+    (outputs shared over threads).  Rates are per output computed, so they
+    compare with the GPU figures of the same shapes; the pass's tokens/s is
+    extrapolated from the per-row times of its link shapes, and labelled so."""
+    import oracle
+    model, cores = host_cpu()
+    threads = max(1, min(cores, oracle.max_threads()))
     out = {}
-    cases = [("prefill", w.M, w.K, w.N, w.p_zero, w.outlier_frac) for w in synth.PREFILL] + \
-            [("decode", 1, 5120, 17408, 1 / 3, 0.0), ("decode", 1, 17408, 5120, 1 / 3, 0.0)]
-    for kind, M, K, N, p0, outl in cases:
-        rows = 8 if kind == "prefill" else 64
-        t = synth.ternary(31 + K, rows, K, p0)
-        s = synth.scales_f16(31 + K, rows, K)
-        x = synth.activations_bf16(31 + K, M, K, outl)
+
+    def rate(M, K, rows, p0, outl, seed):
+        t = synth.ternary(seed, rows, K, p0)
+        s = synth.scales_f16(seed, rows, K)
+        x = synth.activations_bf16(seed, M, K, outl)
         codes = oracle.encode(t)
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.matmul(x, codes, s, K)
+            oracle.matmul(x, codes, s, K, threads=threads)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
+        return reps, el
+
+    cases = [("prefill", w.M, w.K, w.N, w.p_zero, w.outlier_frac) for w in synth.PREFILL] + \
+            [("decode", 1, 5120, 17408, 1 / 3, 0.0), ("decode", 1, 17408, 5120, 1 / 3, 0.0)]
+    for kind, M, K, N, p0, outl in cases:
+        rows = threads if kind == "prefill" else 16 * threads
+        reps, el = rate(M, K, rows, p0, outl, 31 + K)
         flops = 2.0 * M * rows * K * reps
         byts = (rows * K // 4 + 2 * rows * K // 128 + M * K * 2 + M * rows * 4) * reps
         out[f"{kind}_M{M}_K{K}_N{N}"] = {
-            "GFLOP/s": flops / el / 1e9, "GB/s": byts / el / 1e9, "cores": 1, "kind": "oracle",
+            "GFLOP/s": flops / el / 1e9, "GB/s": byts / el / 1e9, "cores": threads, "kind": "oracle",
             "sample": f"{reps} x ({rows} of {N} output rows, M={M}, full K={K}), {el:.1f} s"}
+    # the 27B-class pass: seconds per output row of each distinct link shape
+    links = synth.chain_links()
+    shapes = sorted(set(links))
+    per_row = {}
+    for (K, N) in shapes:
+        rows = 16 * threads
+        reps, el = rate(1, K, rows, 1 / 3, 0.0, 53 + K + N)
+        per_row[(K, N)] = el / (reps * rows)
+    pass_s = sum(per_row[(K, N)] * N for (K, N) in links)
+    packed = sum(N * K // 4 + 2 * N * K // 128 for (K, N) in links)
+    out["decode_pass_27b_class"] = {
+        "tokens_per_s": 1.0 / pass_s, "s_per_pass": pass_s, "GB/s": packed / pass_s / 1e9,
+        "cores": threads, "kind": "oracle", "cpu_model": model,
+        "sample": f"extrapolated: {len(shapes)} link shapes timed on {16 * threads}-row slices "
+                  f"(about {seconds:.0f} s each), scaled to the {len(links)} links' full row counts"}
+    return out
+
+
+def bench_tiny(tern, torch, synth, steps):
+    """The tiny GEMV (M=1, K=1024, N=1024, binary32 x): the latency of one
+    call with its 0.28 MB of weights resident in L2 (the same weights every
+    step), and, labelled as such, the rate over a rotated pool of copies."""
+    w = synth.TINY
+    seed = 41
+    t = synth.ternary(seed, w.N, w.K)
+    s = synth.scales_f16(seed, w.N, w.K)
+    x = torch.from_numpy(synth.activations_f32(seed, w.M, w.K)).cuda()
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    pool = make_pool(tern, torch, t, s, tern.tern_codes_bytes(w.N, w.K) + tern.tern_scales_bytes(w.N, w.K))
+    P = len(pool)
+
+    def same(i):
+        tern.tern_gemv(x, *pool[0], out=y)
+
+    def rotated(i):
+        tern.tern_gemv(x, *pool[i % P], out=y)
+
+    for i in range(5):
+        same(i)
+    ms_same, _, st_same = time_graph(torch, same, steps)
+    ms_rot, _, _ = time_graph(torch, rotated, steps)
+    us_rot = 1e3 * ms_rot / steps
+    byts = gemv_bytes(w.M, w.K, w.N, 4)
+    return {"latency_us_weights_in_l2": per_step_us(st_same),
+            "rotated_pool_us": us_rot, "rotated_pool_GB/s": byts / (us_rot * 1e-6) / 1e9,
+            "bytes": byts, "pool_copies": P}
+
+
+def bench_floor(tern, torch, synth, steps):
+    """Load-only floor: a kernel that only reads (16-byte loads, several in
+    flight per thread, one store per workgroup) exactly the packed-weight
+    bytes of each decode GEMV shape, launched once per step from a graph over
+    a rotated pool like the GEMV itself.  The best of a few launch shapes is
+    reported: no GEMV over the same bytes, launched once per call, can beat
+    it."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "ternary_weight_g128_amd", "libtern_bench.so"))
+    lib.tern_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.tern_bench_read.restype = ctypes.c_int
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    out = {}
+    for (M, K, N) in ((1, 4096, 12288), (1, 5120, 17408), (1, 17408, 5120)):
+        nbytes = N * K // 4 + 2 * N * K // 128
+        nbytes = (nbytes + 15) // 16 * 16
+        copies = max(2, -(-POOL_BYTES // nbytes))
+        pool = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i & 0xff) for i in range(copies)]
+        best = None
+        for wgs in (256, 512, 768, 1024, 2048):
+            for depth in (1, 2, 4, 8):
+                def fn(i, wgs=wgs, depth=depth):
+                    rc = lib.tern_bench_read(ctypes.c_void_p(pool[i % copies].data_ptr()), nbytes, wgs, depth,
+                                             ctypes.c_void_p(sink.data_ptr()),
+                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    assert rc == 0, rc
+                fn(0)
+                ms, _, _ = time_graph(torch, fn, steps, reps=2)
+                us = 1e3 * ms / steps
+                if best is None or us < best[0]:
+                    best = (us, wgs, depth)
+        us, wgs, depth = best
+        out[f"read_K{K}_N{N}"] = {"bytes": nbytes, "us": us, "GB/s": nbytes / (us * 1e-6) / 1e9,
+                                  "frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                  "workgroups": wgs, "loads_in_flight_per_thread": depth}
+        del pool
+        torch.cuda.empty_cache()
     return out
 
 
@@ -285,7 +489,7 @@ def bench_sweep(tern, torch, synth, steps):
 
             for i in range(5):
                 fn(i)
-            ms, _ = time_graph(torch, fn, steps)
+            ms, _, _ = time_graph(torch, fn, steps)
             us = 1e3 * ms / steps
             gbs = gemv_bytes(M, K, N, 2) / (us * 1e-6) / 1e9
             out[f"M{M}_K{K}_N{N}"] = {"us": us, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
@@ -331,8 +535,8 @@ def bench_t5(tern, torch, synth, steps):
             for i in range(5):
                 fn(i)
                 fn2(i)
-            ms, _ = time_graph(torch, fn, steps)
-            ms2, _ = time_graph(torch, fn2, steps)
+            ms, _, _ = time_graph(torch, fn, steps)
+            ms2, _, _ = time_graph(torch, fn2, steps)
             us, us2 = 1e3 * ms / steps, 1e3 * ms2 / steps
             gbs = t5_gemv_bytes(M, K, N) / (us * 1e-6) / 1e9
             out[f"M{M}_K{K}_N{N}"] = {"us": us, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
@@ -362,7 +566,7 @@ def bench_prefill(tern, torch, synth, steps):
 
         for i in range(3):
             fn(i)
-        ms, _ = time_graph(torch, fn, steps)
+        ms, _, _ = time_graph(torch, fn, steps)
         us = 1e3 * ms / steps
         tf = 2.0 * w.M * w.N * w.K / (us * 1e-6) / 1e12
         out[f"M{w.M}_K{w.K}_N{w.N}"] = {"us": us, "TFLOP/s": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
@@ -411,7 +615,7 @@ def bench_chain(tern, torch, synth, passes=5):
 
     one_pass(0)
     torch.cuda.synchronize()
-    ms, _ = time_graph(torch, one_pass, passes)
+    ms, _, _ = time_graph(torch, one_pass, passes)
     ms_pass = ms / passes
     # the same passes as plain back-to-back launches on the stream (host
     # launch cost included), HIP events around them
@@ -449,9 +653,9 @@ def main():
     if args.workload == "copy":
         print(json.dumps({"copy": bench_copy(torch)}))
         return
-    if args.workload in ("sweep", "prefill"):
-        fn = bench_sweep if args.workload == "sweep" else bench_prefill
-        print(json.dumps({args.workload: fn(tern, torch, synth, args.steps)}))
+    if args.workload in ("sweep", "prefill", "tiny", "floor"):
+        fn = {"sweep": bench_sweep, "prefill": bench_prefill, "tiny": bench_tiny, "floor": bench_floor}
+        print(json.dumps({args.workload: fn[args.workload](tern, torch, synth, args.steps)}))
         return
     if args.workload == "chain":
         print(json.dumps({"chain": bench_chain(tern, torch, synth)}))
@@ -483,6 +687,8 @@ def main():
     }
     if not args.no_secondary:
         line["secondary"] = {
+            "tiny_gemv_latency": bench_tiny(tern, torch, synth, 200),
+            "load_only_floor": bench_floor(tern, torch, synth, 200),
             "decode_sweep_gemv": bench_sweep(tern, torch, synth, 200),
             "prefill_gemm": bench_prefill(tern, torch, synth, 20),
             "decode_pass_27b_class": bench_chain(tern, torch, synth),

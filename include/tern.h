@@ -63,13 +63,17 @@ typedef enum tern_status {
 
 typedef enum tern_dtype {
     TERN_F32 = 0,           /* IEEE binary32 */
-    TERN_BF16 = 1           /* bfloat16 (upper half of binary32) */
+    TERN_BF16 = 1,          /* bfloat16 (upper half of binary32) */
+    TERN_F16 = 2            /* IEEE binary16: named for completeness; no device
+                               call takes it (TERN_EUNSUPPORTED).  The scales
+                               are binary16 bit patterns, passed as uint16. */
 } tern_dtype;
 
 #define TERN_GROUP 128            /* weights per FP16 scale */
 #define TERN_SLOTS_PER_WORD 16    /* 2-bit slots per uint32 code word */
 #define TERN_GEMV_MAX_M 16        /* rows of x one tern_gemv call takes */
 #define TERN_FWHT_MAX_BLOCK 4096  /* largest Hadamard block tern_fwht takes */
+#define TERN_MAX_K 2147483520     /* INT32_MAX - 127: largest K of a device matmul */
 #define TERN_ABI_VERSION 1
 
 /* ABI version of the loaded library (TERN_ABI_VERSION it was built with). */
@@ -232,8 +236,10 @@ tern_status tern_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *co
  * section 3), in natural Sylvester order H[i][l] = (-1)^popcount(i & l):
  *   inverse == 0:  y[m, jb+i] = b^-1/2 sum_l H[i][l] d[jb+l] x[m, jb+l]
  *   inverse != 0:  y[m, jb+i] = d[jb+i] b^-1/2 sum_l H[i][l] x[m, jb+l]
- * x: [M][K] TERN_F32 or TERN_BF16; signs: int8 [K] of +-1 (16-byte aligned), or NULL for all +1
- * (other values are multiplied in as given); y: float [M][K], which may be
+ * x: [M][K] TERN_F32 or TERN_BF16; signs: int8 [K] (16-byte aligned), or NULL for all +1.
+ * Only the sign bit of each entry is read: d[k] = -1 where signs[k] < 0 and
+ * d[k] = +1 otherwise (so +1 and -1 mean what they say, 0 counts as +1, and
+ * the transform stays exactly orthonormal); y: float [M][K], which may be
  * the same buffer as x when xdt == TERN_F32.  block: a power of two in
  * [1, 4096]; K % block == 0.  x and y 16-byte aligned.
  * Accuracy: within 1e-5 relative L2 error per row of the exact transform.
@@ -250,8 +256,9 @@ tern_status tern_fwht(const void *x, int xdt, const int8_t *signs, int64_t M, in
  * ydt (TERN_F32, or TERN_BF16 rounded to nearest even), aligned to its dtype.
  * Accuracy: |y - exact| <= 1e-4 * sum_k |s_g t x_k| per element (binary32
  * output; a bfloat16 output adds its own rounding).
- * Errors: TERN_EINVAL (M > 16, sizes, alignment, NULL), TERN_EUNSUPPORTED
- * (dtype), TERN_EDEVICE. */
+ * K <= TERN_MAX_K.
+ * Errors: TERN_EINVAL (M > 16, K > TERN_MAX_K, sizes, alignment, NULL),
+ * TERN_EUNSUPPORTED (dtype), TERN_EDEVICE. */
 tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K,
                       const uint32_t *codes, const uint16_t *scales, int64_t N,
                       void *y, int ydt, void *stream);
@@ -273,8 +280,9 @@ tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uin
  * "Ternary-Bonsai-2-9B-2bit" article (section 3) folds into the stored
  * weights; every workgroup applies it to x in LDS while the code stream is
  * already in flight, so the rotated activations never go to memory.
- * x: [M][K] TERN_F32 or TERN_BF16, 16-byte aligned; signs: int8 [K] of +-1
- * (16-byte aligned) or NULL; block: a power of two in [16, 4096] with
+ * x: [M][K] TERN_F32 or TERN_BF16, 16-byte aligned; signs: int8 [K]
+ * (16-byte aligned) or NULL, read as in tern_fwht (d[k] = -1 where
+ * signs[k] < 0, else +1); block: a power of two in [16, 4096] with
  * K % block == 0; M <= 16; codes, scales, y, ydt as tern_gemv.
  * Accuracy: within tern_gemv's bound for the exact rotation plus
  * sum_k |s_g t| |x'_k - exact x'_k| (the rotation is computed to binary32

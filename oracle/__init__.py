@@ -33,7 +33,7 @@ def build(force: bool = True) -> str:
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
-             "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+             "-ffp-contract=off", "-fopenmp", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -56,6 +56,8 @@ def lib():
         L.oracle_decode.argtypes = [P, I64, I64, P]
         L.oracle_encode.argtypes = [P, I64, I64, P]
         L.oracle_matmul.argtypes = [P, ctypes.c_int, I64, I64, P, P, I64, P, P]
+        L.oracle_matmul_threaded.argtypes = [P, ctypes.c_int, I64, I64, P, P, I64, P, P, ctypes.c_int]
+        L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_matmul_at.argtypes = [P, ctypes.c_int, I64, P, P, P, P, I64, P, P]
         L.oracle_hadamard_entry.argtypes = [I64, I64]
         L.oracle_hadamard_entry.restype = ctypes.c_double
@@ -126,12 +128,19 @@ def _x_and_code(x: np.ndarray):
     raise TypeError(f"unsupported activation dtype {x.dtype}")
 
 
-def matmul(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, K: int):
+def max_threads() -> int:
+    """Host threads the threaded oracle may use (OpenMP's default)."""
+    return lib().oracle_max_threads()
+
+
+def matmul(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, K: int, threads: int = 1):
     """y[m, n] = sum_k s_g t[n, k] x[m, k] in double, and the error scale
     B[m, n] = sum_k |s_g t[n, k] x[m, k]|.
 
     x: float32 [M, K], uint16 bfloat16 bits [M, K] or float64 [M, K];
     codes: uint32 [N, K/16]; scales: uint16 binary16 bits [N, K/128].
+    threads > 1 shares the outputs over host threads; every output is the
+    same k-ordered sum, so the result is bit-identical to threads = 1.
     """
     x, xdt = _x_and_code(x)
     M = x.shape[0]
@@ -141,8 +150,12 @@ def matmul(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, K: int):
     N = codes.shape[0]
     y = np.zeros((M, N), dtype=np.float64)
     b = np.zeros((M, N), dtype=np.float64)
-    rc = lib().oracle_matmul(_ptr(x), xdt, M, K, _ptr(codes), _ptr(scales), N,
-                             _ptr(y), _ptr(b))
+    if threads > 1:
+        rc = lib().oracle_matmul_threaded(_ptr(x), xdt, M, K, _ptr(codes), _ptr(scales), N,
+                                          _ptr(y), _ptr(b), int(threads))
+    else:
+        rc = lib().oracle_matmul(_ptr(x), xdt, M, K, _ptr(codes), _ptr(scales), N,
+                                 _ptr(y), _ptr(b))
     if rc:
         raise ValueError("slot value 3 is not a ternary code")
     return y, b

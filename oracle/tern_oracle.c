@@ -30,6 +30,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_GROUP 128   /* [MC] Weight representation: 128 weights per FP16 scale */
 #define ORACLE_SLOTS 16    /* 2-bit slots per 32-bit word ([MC] Memory requirement) */
@@ -152,6 +155,35 @@ int oracle_matmul(const void *x, int xdt, int64_t M, int64_t K,
             rc |= one_output(x, xdt, K, codes, scales, m, n,
                              &y[m * N + n], &bound[m * N + n]);
     return rc;
+}
+
+/* oracle_matmul with its (m, n) outputs shared out over `threads` host
+ * threads (OpenMP, static partition).  Each output is still one_output: the
+ * same k loop in the same order, so the result is bit-identical to
+ * oracle_matmul for any thread count; only which thread computes an output
+ * changes. */
+int oracle_matmul_threaded(const void *x, int xdt, int64_t M, int64_t K,
+                           const uint32_t *codes, const uint16_t *scales, int64_t N,
+                           double *y, double *bound, int threads)
+{
+    int rc = 0;
+    const int64_t total = M * N;
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1) reduction(| : rc)
+    for (int64_t i = 0; i < total; ++i) {
+        const int64_t m = i / N, n = i % N;
+        rc |= one_output(x, xdt, K, codes, scales, m, n, &y[m * N + n], &bound[m * N + n]);
+    }
+    return rc;
+}
+
+/* The number of host threads an OpenMP region may use here. */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* The same definition at a list of (m, n) output positions only. */

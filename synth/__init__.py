@@ -94,6 +94,15 @@ def signs(seed: int, K: int) -> np.ndarray:
     return np.where(r.random(K) < 0.5, -1, 1).astype(np.int8)
 
 
+def sign_bytes(seed: int, K: int) -> np.ndarray:
+    """int8 [K] drawn from the whole int8 range, with 0, +-1, +-2, -128 and
+    127 each drawn often: sign vectors whose entries are not all +-1."""
+    r = _rng(seed, _S_SIGNS)
+    special = np.array([0, 1, -1, 2, -2, -128, 127], dtype=np.int16)
+    v = np.where(r.random(K) < 0.5, special[r.integers(0, len(special), K)], r.integers(-128, 128, K))
+    return v.astype(np.int8)
+
+
 # ---------------------------------------------------------------------------
 # Named workloads (shapes of one 27B-class projection and its neighbours)
 # ---------------------------------------------------------------------------

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtern.so")
 
 TERN_OK, TERN_EINVAL, TERN_ENOTTERNARY, TERN_EBADCODE, TERN_EUNSUPPORTED, TERN_EDEVICE = range(6)
-TERN_F32, TERN_BF16 = 0, 1
+TERN_F32, TERN_BF16, TERN_F16 = 0, 1, 2
+TERN_MAX_K = 2147483520
 TERN_GROUP = 128
 TERN_GEMV_MAX_M = 16
 TERN_FWHT_MAX_BLOCK = 4096
@@ -340,13 +341,46 @@ def _dev_ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape_check(where, name, t, shape, sizes, device):
+    """Raise ValueError unless tensor t has the given shape, an element size
+    in `sizes` and lives on `device` (marshalling only: nothing is computed)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.element_size() not in sizes:
+        raise ValueError(f"{where}: {name} has dtype {t.dtype} (element size {t.element_size()}), "
+                         f"expected element size {sizes}")
+    if t.device != device:
+        raise ValueError(f"{where}: {name} is on {t.device}, expected {device}")
+
+
+def _matrix_shapes(where, x, K, codes, scales, out, M, N, out_sizes=(2, 4)):
+    """Check packed weights [N, K/16] (4-byte words), scales [N, K/128]
+    (2-byte binary16 bits) and the output [M, N] against x [M, K]."""
+    if K % TERN_GROUP:
+        raise ValueError(f"{where}: K = {K} is not a multiple of {TERN_GROUP}")
+    _shape_check(where, "codes", codes, (N, K // 16), (4,), x.device)
+    _shape_check(where, "scales", scales, (N, K // TERN_GROUP), (2,), x.device)
+    _shape_check(where, "out", out, (M, N), out_sizes, x.device)
+
+
+def _dims2(where, x):
+    if x.dim() != 2:
+        raise ValueError(f"{where}: x must be 2-D [M, K], got {tuple(x.shape)}")
+    return x.shape
+
+
 def tern_pack_device(t, out=None, stream=None):
     """t: int8 [N, K] on the GPU, values in {-1, 0, 1} (not checked) ->
     codes int32 [N, K/16] (bit patterns of the uint32 words)."""
     torch = _torch()
-    N, K = t.shape
+    N, K = _dims2("tern_pack_device", t)
+    if K % TERN_GROUP:
+        raise ValueError(f"tern_pack_device: K = {K} is not a multiple of {TERN_GROUP}")
+    if t.element_size() != 1:
+        raise ValueError("tern_pack_device: t must be int8")
     if out is None:
         out = torch.empty((N, K // 16), dtype=torch.int32, device=t.device)
+    _shape_check("tern_pack_device", "out", out, (N, K // 16), (4,), t.device)
     _check(_lib.tern_pack_device(_dev_ptr(t), N, K, _dev_ptr(out), _stream_ptr(stream)), "tern_pack_device")
     return out
 
@@ -356,9 +390,12 @@ def tern_fwht(x, signs, block: int, inverse: bool = False, out=None, stream=None
     x: [M, K] float32 or bfloat16; signs: int8 [K] or None; returns float32
     [M, K] (out may be x itself when x is float32)."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims2("tern_fwht", x)
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _shape_check("tern_fwht", "out", out, (M, K), (4,), x.device)
+    if signs is not None:
+        _shape_check("tern_fwht", "signs", signs, (K,), (1,), x.device)
     _check(_lib.tern_fwht(_dev_ptr(x), _dt(x), _dev_ptr(signs), M, K, block, int(bool(inverse)),
                           _dev_ptr(out), _stream_ptr(stream)), "tern_fwht")
     return out
@@ -368,10 +405,11 @@ def tern_gemv(x, codes, scales, out=None, out_dtype=None, stream=None):
     """y[M, N] = x[M, K] (s_g t)^T for M <= 16.  codes int32 [N, K/16] (bit
     patterns of the uint32 words), scales int16 [N, K/128] (binary16 bits)."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims2("tern_gemv", x)
     N = codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    _matrix_shapes("tern_gemv", x, K, codes, scales, out, M, N)
     _check(_lib.tern_gemv(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
                           _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv")
     return out
@@ -382,10 +420,13 @@ def tern_rotate_gemv(x, signs, block: int, codes, scales, out=None, out_dtype=No
     blocks of `block` along K (forward).  x: [M, K] float32 or bfloat16,
     M <= 16; signs int8 [K] or None."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims2("tern_rotate_gemv", x)
     N = codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    _matrix_shapes("tern_rotate_gemv", x, K, codes, scales, out, M, N)
+    if signs is not None:
+        _shape_check("tern_rotate_gemv", "signs", signs, (K,), (1,), x.device)
     _check(_lib.tern_rotate_gemv(_dev_ptr(x), _dt(x), _dev_ptr(signs), block, M, K, _dev_ptr(codes),
                                  _dev_ptr(scales), N, _dev_ptr(out), _dt(out), _stream_ptr(stream)),
            "tern_rotate_gemv")
@@ -396,10 +437,15 @@ def tern_gemv_t5(x, data, scales, out=None, out_dtype=None, stream=None):
     """y [M, N] = x [M, K] (bfloat16, M <= 16) times the base-3 weights (data
     uint8 [N, ceil(K/640) * 128] on the device) with their group scales."""
     T = _torch()
-    M, K = x.shape
+    M, K = _dims2("tern_gemv_t5", x)
     N = data.shape[0]
+    if K % TERN_GROUP:
+        raise ValueError(f"tern_gemv_t5: K = {K} is not a multiple of {TERN_GROUP}")
     if out is None:
         out = T.empty((M, N), dtype=out_dtype or T.float32, device=x.device)
+    _shape_check("tern_gemv_t5", "data", data, (N, ((K // TERN_GROUP) + 4) // 5 * 128), (1,), x.device)
+    _shape_check("tern_gemv_t5", "scales", scales, (N, K // TERN_GROUP), (2,), x.device)
+    _shape_check("tern_gemv_t5", "out", out, (M, N), (2, 4), x.device)
     _check(_lib.tern_gemv_t5(_dev_ptr(x), _dt(x), M, K, _dev_ptr(data), _dev_ptr(scales), N,
                              _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv_t5")
     return out
@@ -412,13 +458,16 @@ def tern_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 def tern_gemm(x, codes, scales, out=None, workspace=None, stream=None):
     """y[M, N] = x[M, K] (s_g t)^T, bfloat16 x, any M."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims2("tern_gemm", x)
     N = codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _matrix_shapes("tern_gemm", x, K, codes, scales, out, M, N, out_sizes=(4,))
     need = tern_gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None and workspace.device != x.device:
+        raise ValueError(f"tern_gemm: workspace is on {workspace.device}, expected {x.device}")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.tern_gemm(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
                           _dev_ptr(out), _dev_ptr(workspace), ws_bytes, _stream_ptr(stream)),

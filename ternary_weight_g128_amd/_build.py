@@ -9,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtern.so")
+BENCH_LIB = os.path.join(HERE, "libtern_bench.so")  # measurement helper, not the matmul path
 
 # (source, extra flags).  The GEMM keeps its MFMA accumulators in ordinary
 # VGPRs: it rescales them every 128-K group, and accumulator registers would
@@ -68,6 +69,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's read-only streaming kernel, a library of its own
+    tmpb = BENCH_LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, "-shared", os.path.join(CSRC, "tern_bench.hip"), "-o", tmpb], verbose)
+    os.replace(tmpb, BENCH_LIB)
     return LIB
 
 

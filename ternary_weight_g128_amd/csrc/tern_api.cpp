@@ -31,6 +31,11 @@ tern_status check_matmul_args(const char *fn, const void *x, int xdt, int64_t M,
         set_error(std::string(fn) + ": K must be a multiple of 128 (whole scale groups)");
         return TERN_EINVAL;
     }
+    if (K > TERN_MAX_K) {
+        // the kernels index K and the groups of a row in 32-bit integers
+        set_error(std::string(fn) + ": K above TERN_MAX_K (" + std::to_string(TERN_MAX_K) + ")");
+        return TERN_EINVAL;
+    }
     if (xdt != TERN_F32 && xdt != TERN_BF16) {
         set_error(std::string(fn) + ": activation dtype must be TERN_F32 or TERN_BF16");
         return TERN_EUNSUPPORTED;

@@ -91,6 +91,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 template <class Kernel>
 int ensure_lds(Kernel kernel, size_t bytes)
 {
+    if (bytes > kMaxLds) return (int)hipErrorInvalidValue;  // more than one workgroup's LDS
     if (bytes <= 65536) return 0;
     static std::mutex mu;
     static std::set<std::pair<const void *, int>> granted;

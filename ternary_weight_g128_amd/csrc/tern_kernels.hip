@@ -23,6 +23,7 @@
 #include <cstdint>
 #include <mutex>
 #include <set>
+#include <type_traits>
 #include <utility>
 
 #include "tern_internal.h"
@@ -39,6 +40,20 @@ typedef const u32x4_t __attribute__((address_space(1))) gu32x4_t;  // global mem
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef const u32x2_t __attribute__((address_space(1))) gu32x2_t;
 typedef const uint32_t __attribute__((address_space(1))) gu32_t;
+
+// Sign vectors: only the sign bit of each int8 entry is read, so d[k] = -1
+// where signs[k] < 0 and +1 otherwise.  Every transform path applies d by
+// flipping the binary32 (or bfloat16) sign bit, which is exact.
+// Bit 31 set iff byte j of the four sign bytes in `w` is negative.
+__device__ __forceinline__ uint32_t sign_bit(uint32_t w, int j)
+{
+    return ((w >> (8 * j + 7)) & 1u) << 31;
+}
+
+__device__ __forceinline__ float flip_if(float v, uint32_t bit31)
+{
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ bit31);
+}
 
 
 
@@ -207,6 +222,30 @@ __device__ __forceinline__ void h64_slice(const void *xs, int jt, int c, int g, 
 // where element e of (G, mu, g) holds k = 128 G + 16 w + 4 h + (e >> 1) +
 // 8 (e & 1) for the word w = 2 {0, 2, 1, 3}[g] + (mu >> 1).
 
+// Eight consecutive binary32 activations (one MFMA A operand's worth).
+struct F32x8 {
+    u32x4_t v[2];
+};
+
+// The bfloat16 part of eight binary32 values that one A row carries: the
+// rounding of each value (lo == false) or the rounding of its remainder
+// (lo == true; x - hi is exact in binary32, and hi + lo carries 16
+// significand bits of x).
+__device__ __forceinline__ bf16x8_t split_part(const F32x8 &f, bool lo)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    u32x4_t out;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float f0 = __builtin_bit_cast(float, f.v[v >> 1][2 * (v & 1)]);
+        const float f1 = __builtin_bit_cast(float, f.v[v >> 1][2 * (v & 1) + 1]);
+        const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
+        const bf16x2_t pl = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
+        out[v] = lo ? __builtin_bit_cast(uint32_t, pl) : __builtin_bit_cast(uint32_t, ph);
+    }
+    return __builtin_bit_cast(bf16x8_t, out);
+}
+
 struct GemvArgs {
     const void *x;
     const uint32_t *codes;
@@ -352,7 +391,7 @@ template <int MX, bool XF32, int TPW, bool SC4, int ROT = 0, int ROTL = 0, bool 
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 {
     static_assert(ROT == 0 || XF32, "rotated activations are staged as hi/lo rows");
-    static_assert(!AG || (!XF32 && ROT == 0), "direct A loads take bfloat16 activations");
+    static_assert(!AG || ROT == 0, "direct A loads take unrotated activations");
     constexpr int PF = 4;
     constexpr int kDist = 2;  // blocks of codes in flight
     constexpr bool kQuadScales = MX <= 4;
@@ -396,7 +435,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     // thread a staging unit; the loads below are unconditional so that the
     // compiler can count outstanding loads exactly.
     __bf16 *lds_x = reinterpret_cast<__bf16 *>(smem);
-    const int rowpad = a.K + (a.K >> 4);  // padded row of the rotation scratch
+    const int rowpad = ROT ? a.K + (a.K >> 4) : 0;  // padded row of the rotation scratch
     float *rot = reinterpret_cast<float *>(smem + (AG ? 0 : (size_t)a.K * MX * 2));
     float *red = rot + (ROT ? (size_t)a.M * rowpad : 0);
 
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     //    Unit indices past the end are clamped to the last unit: duplicate
     //    stores write the same values to the same LDS bytes.
     const int wpr = a.K / 16;  // words (units) per activation row
-    const int units = a.M * wpr;
+    const int units = AG ? 0 : a.M * wpr;
     const int nthreads = 64 * waves;
     constexpr bool kInF32 = ROT ? (ROT == 2) : XF32;
     // 4096-point blocks go through the matrix cores (rot_unit below); other
@@ -425,7 +464,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     const int rot_per_row = (a.K >> 12) * 4;
     const int rot_units = a.M * rot_per_row;
     constexpr int kPadX = ROT == 2 ? 68 : 72;
-    const int xs_row = (a.K >> 6) * kPadX;  // elements per staged row
+    const int xs_row = kMfmaRot ? (a.K >> 6) * kPadX : 0;  // elements per staged row
 #pragma unroll
     for (int i = 0; i < (AG ? 0 : kUB); ++i) {
         int u = threadIdx.x + i * nthreads;
@@ -530,8 +569,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             float v[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float sg = (float)(int8_t)((dv[e >> 2] >> (8 * (e & 3))) & 0xffu);
-                v[e] = __builtin_bit_cast(float, xv.v[e]) * sg;
+                v[e] = __builtin_bit_cast(float, xv.v[e] ^ sign_bit(dv[e >> 2], e & 3));
             }
             butterfly_bits(v, 0, 4);
             float *row = rot + (size_t)m * rowpad + 17 * wi;  // pad(16 wi + e) = 17 wi + e
@@ -660,11 +698,19 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
     constexpr int kGroupStride = 16 * MX * 8;  // bf16 elements per staged group
     constexpr int kMuStride = 4 * MX * 8;
     // AG: A operands of the two groups of a block, loaded one block ahead
-    bf16x8_t ag[2][8];
-    // lanes whose A row does not exist load row Mx - 1 (always in bounds): their
-    // output rows are never stored, and no select or branch is needed per load
-    const __bf16 *xrow = static_cast<const __bf16 *>(a.x) + (int64_t)(a_active ? arow : Mx - 1) * a.K +
-                         32 * (((g & 1) << 1) | (g >> 1));
+    // (binary32 input: the eight raw values, split into a bfloat16 part when
+    // they are consumed: A row 2m takes the high part of x[m], row 2m + 1 the
+    // remainder, as in the staged image)
+    typedef typename std::conditional<XF32, F32x8, bf16x8_t>::type AgT;
+    AgT ag[2][8];
+    const bool lo_part = XF32 && (arow & 1);
+    // lanes whose A row does not exist load the last row of x (always in
+    // bounds): their output rows are never stored, and no select or branch is
+    // needed per load
+    const int xr = a_active ? (XF32 ? arow >> 1 : arow) : a.M - 1;
+    const int xcol = 32 * (((g & 1) << 1) | (g >> 1));
+    const __bf16 *xrow = static_cast<const __bf16 *>(a.x) + (int64_t)xr * a.K + xcol;
+    const float *xrow_f = static_cast<const float *>(a.x) + (int64_t)xr * a.K + xcol;
     auto load_a = [&](int b, int slot) {
         if constexpr (AG) {
             b = b < nblocks ? b : nblocks - 1;
@@ -672,8 +718,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
             const int gl1 = (gl0 + 1 < g_end) ? gl0 + 1 : gl0;
 #pragma unroll
             for (int mu = 0; mu < 4; ++mu) {
-                ag[slot][mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu);
-                ag[slot][4 + mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu);
+                if constexpr (XF32) {
+                    const u32x4_t *s0 = reinterpret_cast<const u32x4_t *>(xrow_f + 128 * gl0 + 8 * mu);
+                    const u32x4_t *s1 = reinterpret_cast<const u32x4_t *>(xrow_f + 128 * gl1 + 8 * mu);
+                    ag[slot][mu].v[0] = s0[0];
+                    ag[slot][mu].v[1] = s0[1];
+                    ag[slot][4 + mu].v[0] = s1[0];
+                    ag[slot][4 + mu].v[1] = s1[1];
+                } else {
+                    ag[slot][mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu);
+                    ag[slot][4 + mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu);
+                }
             }
         }
     };
@@ -689,8 +744,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
         if constexpr (AG) {
 #pragma unroll
             for (int mu = 0; mu < 4; ++mu) {
-                a0[mu] = ag[p & 1][mu];
-                a1[mu] = ag[p & 1][4 + mu];
+                if constexpr (XF32) {
+                    a0[mu] = split_part(ag[p & 1][mu], lo_part);
+                    a1[mu] = split_part(ag[p & 1][4 + mu], lo_part);
+                } else {
+                    a0[mu] = ag[p & 1][mu];
+                    a1[mu] = ag[p & 1][4 + mu];
+                }
             }
             load_a(b + 1, (p + 1) & 1);
         } else if (a_active) {
@@ -883,7 +943,7 @@ __global__ __launch_bounds__(256) void fwht16_kernel(
             if (!inverse && signs) {
                 const u32x4_t d = *reinterpret_cast<const u32x4_t *>(signs + sbase + 16 * t);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) v[r] *= (float)(int8_t)((d[r >> 2] >> (8 * (r & 3))) & 0xffu);
+                for (int r = 0; r < 16; ++r) v[r] = flip_if(v[r], sign_bit(d[r >> 2], r & 3));
             }
         } else {
 #pragma unroll
@@ -908,7 +968,7 @@ __global__ __launch_bounds__(256) void fwht16_kernel(
             for (int r = 0; r < 16; ++r) {
                 const int i = fwht_index(t, r, rb);
                 float o = v[r] * norm;
-                if (inverse && signs) o *= (float)signs[sbase + i];
+                if (inverse && signs) o = flip_if(o, sign_bit((uint32_t)(uint8_t)signs[sbase + i], 0));
                 y[m * K + sbase + i] = o;
             }
         }
@@ -971,7 +1031,7 @@ __global__ __launch_bounds__(256) void fwht4096_kernel(const void *__restrict__ 
             for (int r = 0; r < 4; ++r) {
                 const int i = 64 * (16 * ot + 4 * g + r) + 16 * wave + c;
                 float v = o[ot][r] * norm;
-                if (inverse && signs) v *= (float)signs[k0 + i];
+                if (inverse && signs) v = flip_if(v, sign_bit((uint32_t)(uint8_t)signs[k0 + i], 0));
                 y[m * K + k0 + i] = v;
             }
         __syncthreads();  // the next row's staging reuses the LDS block
@@ -997,7 +1057,7 @@ __global__ __launch_bounds__(256) void fwht_small_kernel(
             if (r < b) {
                 v[r] = XF32 ? static_cast<const float *>(x)[base + r]
                             : bf16_to_float(static_cast<const uint16_t *>(x)[base + r]);
-                if (!inverse && signs) v[r] *= (float)signs[sb + r];
+                if (!inverse && signs) v[r] = flip_if(v[r], sign_bit((uint32_t)(uint8_t)signs[sb + r], 0));
             }
         }
 #pragma unroll
@@ -1016,7 +1076,7 @@ __global__ __launch_bounds__(256) void fwht_small_kernel(
         for (int r = 0; r < 8; ++r) {
             if (r < b) {
                 float o = v[r] * norm;
-                if (inverse && signs) o *= (float)signs[sb + r];
+                if (inverse && signs) o = flip_if(o, sign_bit((uint32_t)(uint8_t)signs[sb + r], 0));
                 y[base + r] = o;
             }
         }
@@ -1060,12 +1120,12 @@ inline GemvPlan plan_gemv(int64_t N, int64_t K, int mx)
 // for LDS): direct A loads, so LDS does not cap the workgroups per CU.  Two
 // tiles per wave (four spill registers) and two K-waves, four for long rows,
 // from sweeps of tiles per wave x tile-waves x K-waves at M = 8 and 16.
-inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx)
+inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx, bool x_f32)
 {
     const int64_t tiles = (N + kTileN - 1) / kTileN;
     const int nblk = (int)((K / kGroup + 1) / 2);
     GemvPlan pl;
-    pl.tpw = 2;
+    pl.tpw = x_f32 ? 1 : 2;  // binary32 operands in flight take twice the registers
     const int64_t tile_groups = (tiles + pl.tpw - 1) / pl.tpw;
     pl.wt = 1;
     pl.wk = nblk >= 32 ? 4 : 2;  // 5120 -> 17408: 21.3 -> 20.5 us at M = 8
@@ -1081,9 +1141,10 @@ int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
     const bool sc4 = (a.K / kGroup) % 2 == 0;
     void (*kernel)(GemvArgs) = sc4 ? gemv_kernel<MX, XF32, TPW, true> : gemv_kernel<MX, XF32, TPW, false>;
-    if constexpr (!XF32)
+    // binary32 direct loads run one tile per wave (two would spill registers)
+    if constexpr (!(XF32 && TPW > 1))
         if (pl.ag)
-            kernel = sc4 ? gemv_kernel<MX, false, TPW, true, 0, 0, true> : gemv_kernel<MX, false, TPW, false, 0, 0, true>;
+            kernel = sc4 ? gemv_kernel<MX, XF32, TPW, true, 0, 0, true> : gemv_kernel<MX, XF32, TPW, false, 0, 0, true>;
     int rc = ensure_lds(kernel, pl.lds);
     if (rc) return rc;
     a.wk = pl.wk;
@@ -1110,7 +1171,9 @@ int launch_gemv_x(GemvArgs a, hipStream_t stream)
     const int Mx = XF32 ? 2 * a.M : a.M;
     const int mx = Mx <= 1 ? 1 : Mx <= 2 ? 2 : Mx <= 4 ? 4 : Mx <= 8 ? 8 : 16;
     GemvPlan pl = plan_gemv(a.N, a.K, mx);
-    if (!XF32 && (mx >= 8 || pl.lds > kMaxLds)) pl = plan_gemv_ag(a.N, a.K, mx);
+    // direct A loads: bfloat16 with eight or more A rows, or any input whose
+    // staged image would not fit in LDS
+    if ((!XF32 && mx >= 8) || pl.lds > kMaxLds) pl = plan_gemv_ag(a.N, a.K, mx, XF32);
     switch (mx) {
     case 1: return launch_gemv_mx<1, XF32>(a, pl, stream);
     case 2: return launch_gemv_mx<2, XF32>(a, pl, stream);
@@ -1176,9 +1239,9 @@ inline int gemv_rows_per_launch(int64_t N, int64_t K, bool x_f32)
 {
     if (!x_f32) return 16;  // bfloat16: direct A loads where the staged image would not fit
     const int per = 2;
-    for (int rows = 16 / per; rows > 1; rows /= 2)
+    for (int rows = 16 / per; rows >= 1; rows /= 2)
         if (plan_gemv(N, K, rows * per).lds <= kMaxLds) return rows;
-    return 1;
+    return 16 / per;  // not even one row fits: direct A loads, eight rows per launch
 }
 
 // ---------------------------------------------------------------------------

@@ -186,3 +186,101 @@ def test_codec_rejects(tern):
     lib = tern.lib()
     assert lib.tern_pack(None, None, 1, 100, None, None) == tern.TERN_EINVAL
     assert lib.tern_pack(None, None, 0, 128, None, None) == tern.TERN_OK
+
+
+# K above TERN_MAX_K (INT32_MAX - 127) is rejected before any launch: the
+# kernels index K in 32-bit integers.  N = 1 keeps N * K / 16 below the
+# separate size cap, so only the K bound can fire.
+BIG_K = 1 << 31
+
+
+def test_k_bound_constant(tern):
+    assert tern.TERN_MAX_K == 2 ** 31 - 1 - 127
+    assert tern.TERN_MAX_K % 128 == 0
+
+
+@pytest.mark.parametrize("call", ["gemv", "rotate_gemv", "gemm"])
+def test_matmul_rejects_k_above_int32(tern, call):
+    if call == "gemv":
+        st = _gemv(tern, K=BIG_K, N=1)
+        ok = _gemv(tern, K=tern.TERN_MAX_K + 128, N=1)
+    elif call == "rotate_gemv":
+        st = _rot(tern, K=BIG_K, N=1)
+        ok = _rot(tern, K=tern.TERN_MAX_K + 128, N=1)
+    else:
+        st = _gemm(tern, K=BIG_K, N=1)
+        ok = _gemm(tern, K=tern.TERN_MAX_K + 128, N=1)
+    assert st == tern.TERN_EINVAL and ok == tern.TERN_EINVAL
+    assert "K" in tern.tern_last_error()
+
+
+def test_f16_dtype_is_named_and_unsupported(tern):
+    assert tern.TERN_F16 == 2
+    assert _gemv(tern, xdt=tern.TERN_F16) == tern.TERN_EUNSUPPORTED
+    assert _gemv(tern, ydt=tern.TERN_F16) == tern.TERN_EUNSUPPORTED
+    assert _fwht(tern, xdt=tern.TERN_F16) == tern.TERN_EUNSUPPORTED
+    assert _rot(tern, xdt=tern.TERN_F16) == tern.TERN_EUNSUPPORTED
+    assert _gemm(tern, xdt=tern.TERN_F16) == tern.TERN_EUNSUPPORTED
+
+
+# The Python wrappers check shapes, element sizes and devices before the C
+# call (argument marshalling; a mismatch would otherwise reach the kernels as
+# out-of-bounds addresses).  CPU tensors suffice: the check fires first.
+
+def _torch():
+    import torch
+    return torch
+
+
+def _w(N, K):
+    T = _torch()
+    return T.zeros((N, K // 16), dtype=T.int32), T.zeros((N, K // 128), dtype=T.int16)
+
+
+@pytest.mark.parametrize("bad", ["codes_rows", "codes_cols", "scales", "out", "codes_dtype", "x_3d", "k"])
+def test_gemv_wrapper_checks_shapes(tern, bad):
+    T = _torch()
+    M, K, N = 2, 256, 32
+    x = T.zeros((M, K), dtype=T.bfloat16)
+    codes, scales = _w(N, K)
+    out = T.zeros((M, N), dtype=T.float32)
+    if bad == "codes_rows":
+        scales = T.zeros((N + 1, K // 128), dtype=T.int16)
+        codes = T.zeros((N + 1, K // 16 + 1), dtype=T.int32)
+    elif bad == "codes_cols":
+        codes = T.zeros((N, K // 16 - 1), dtype=T.int32)
+    elif bad == "scales":
+        scales = T.zeros((N, K // 128 + 1), dtype=T.int16)
+    elif bad == "out":
+        out = T.zeros((M, N + 1), dtype=T.float32)
+    elif bad == "codes_dtype":
+        codes = T.zeros((N, K // 16), dtype=T.int16)
+    elif bad == "x_3d":
+        x = T.zeros((1, M, K), dtype=T.bfloat16)
+    elif bad == "k":
+        x = T.zeros((M, 200), dtype=T.bfloat16)
+    with pytest.raises(ValueError):
+        tern.tern_gemv(x, codes, scales, out=out)
+
+
+def test_other_wrappers_check_shapes(tern):
+    T = _torch()
+    M, K, N = 2, 4096, 16
+    x = T.zeros((M, K), dtype=T.bfloat16)
+    codes, scales = _w(N, K)
+    with pytest.raises(ValueError, match="signs"):
+        tern.tern_rotate_gemv(x, T.ones(K - 1, dtype=T.int8), 4096, codes, scales)
+    with pytest.raises(ValueError, match="scales"):
+        tern.tern_rotate_gemv(x, None, 4096, codes, scales[:, :-1])
+    with pytest.raises(ValueError, match="signs"):
+        tern.tern_fwht(x, T.ones(K, dtype=T.int16), 4096)
+    with pytest.raises(ValueError, match="out"):
+        tern.tern_fwht(x, None, 4096, out=T.zeros((M, K), dtype=T.bfloat16))
+    with pytest.raises(ValueError, match="out"):
+        tern.tern_gemm(x, codes, scales, out=T.zeros((M, N), dtype=T.bfloat16))
+    with pytest.raises(ValueError, match="codes"):
+        tern.tern_gemm(x, codes[:, 1:], scales)
+    with pytest.raises(ValueError, match="data"):
+        tern.tern_gemv_t5(x, T.zeros((N, 100), dtype=T.uint8), scales)
+    with pytest.raises(ValueError, match="out"):
+        tern.tern_pack_device(T.zeros((N, K), dtype=T.int8), out=T.zeros((N, K // 8), dtype=T.int32))

@@ -571,3 +571,48 @@ def test_t5_accounting(oracle_lib):
     assert info < oracle_lib.t5_bits_per_weight(1, 640) < g["deployed_bits_per_weight"]
     # a ragged tail costs a whole superblock: K = 4096 is 7 superblocks for 32 groups
     assert oracle_lib.t5_bits_per_weight(1, 4096) == 8 * (7 * 128 + 64) / 4096
+
+
+# ---------------------------------------------------------------------------
+# Threaded oracle matmul: the outputs shared out over host threads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("threads", [2, 3, 8])
+def test_threaded_matmul_bit_identical_to_serial(oracle_lib, threads):
+    # each output is the same k-ordered double sum, whichever thread runs it
+    M, K, N = 3, 1280, 97
+    t = synth.ternary(41, N, K)
+    s = synth.scales_f16(41, N, K)
+    x = synth.activations_bf16(41, M, K)
+    codes = oracle_lib.encode(t)
+    y1, b1 = oracle_lib.matmul(x, codes, s, K)
+    yt, bt = oracle_lib.matmul(x, codes, s, K, threads=threads)
+    assert np.array_equal(y1, yt) and np.array_equal(b1, bt)
+
+
+def test_threaded_matmul_integer_inputs_exact(oracle_lib):
+    # the integer-exact closed form, through the threaded entry point itself
+    rng = np.random.default_rng(19)
+    M, K, N = 5, 2048, 33
+    t = synth.ternary(19, N, K)
+    s = rng.choice(np.array([0.5, 1.0, 2.0], dtype=np.float16), size=(N, K // 128))
+    x = rng.integers(-64, 65, size=(M, K)).astype(np.float32)
+    y, _ = oracle_lib.matmul(x, oracle_lib.encode(t), s.view(np.uint16), K, threads=4)
+    W2 = t.astype(np.int64) * np.repeat((s.astype(np.float64) * 2).astype(np.int64), 128, axis=1)
+    expect = (x.astype(np.int64) @ W2.T).astype(np.float64) / 2
+    assert np.array_equal(y, expect)
+
+
+def test_threaded_matmul_matches_numpy_dense(oracle_lib):
+    M, K, N = 2, 768, 50
+    t = synth.ternary(23, N, K)
+    s = synth.scales_f16(23, N, K)
+    x = synth.activations_f32(23, M, K)
+    y, b = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=5)
+    W = _dense_from_original(t, s)
+    x64 = x.astype(np.float64)
+    assert np.allclose(y, x64 @ W.T, rtol=0, atol=1e-12 * (np.abs(x64) @ np.abs(W).T).max())
+    with pytest.raises(ValueError):
+        bad = oracle_lib.encode(t)
+        bad[0, 0] |= 3
+        oracle_lib.matmul(x, bad, s, K, threads=3)
