@@ -126,7 +126,7 @@ tern_status tern_rotate_gemv(const void *x, int xdt, const int8_t *signs, int64_
         set_error("tern_rotate_gemv: N too large");
         return TERN_EINVAL;
     }
-    if (tern::rotate_gemv_lds(M, N, K) > tern::max_lds_bytes()) {
+    if (!tern::rotate_gemv_fits(M, N, K, block, xdt == TERN_F32)) {
         set_error("tern_rotate_gemv: M * K too large for one workgroup's LDS; use tern_fwht then "
                   "tern_gemv");
         return TERN_EUNSUPPORTED;

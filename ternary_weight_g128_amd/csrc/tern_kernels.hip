@@ -31,6 +31,7 @@
 namespace {
 
 #include "tern_device.h"
+#include "tern_h64.h"
 
 // Sixteen +1 signs: the sign row read when the caller passes no sign vector,
 // so that the sign load is unconditional (a load under a branch makes the
@@ -84,112 +85,6 @@ __device__ __forceinline__ void butterfly_bits(float (&v)[16], int j_lo, int j_h
     }
 }
 
-// One 16-column slice of a 4096-point transform on the matrix cores.  A
-// block viewed as a 64 x 64 matrix X[i][j] = x[64 i + j] transforms as
-// H64 X H64 (the Sylvester matrix of 4096 points is the Kronecker square of
-// the 64-point one).  The wave computes
-//   Z  = X H64[:, 16 jt + 0..15]   (A = rows of X, B = H64)
-//   X' = H64 Z                     (A = H64, B = Z as three bfloat16 parts)
-// with v_mfma_f32_16x16x32_bf16 and binary32 accumulation.  The contraction
-// order of the second product is the order in which the first leaves Z in
-// the lanes (k-slot e of lane group g at step st is row 32 st + 16 (e >> 2)
-// + 4 g + (e & 3)), so Z never leaves the registers.  +-1 is exact in
-// bfloat16, and hi + mid + lo carry all 24 significand bits of Z.
-// xs: row i of X at element i * (64 + pad) (bfloat16 pairs, or binary32 when
-// IN_F32, which is split into two exact bfloat16 parts for the first
-// product); lane (c = lane & 15, g = lane >> 4); out[ot][r] =
-// X'[16 ot + 4 g + r][16 jt + c], not normalized.
-template <bool IN_F32>
-__device__ __forceinline__ void h64_slice(const void *xs, int jt, int c, int g, f32x4_t (&out)[4])
-{
-    constexpr int kPadX = IN_F32 ? 68 : 72;  // elements per staged row (conflict-free 16-byte reads)
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    auto pm1 = [](uint32_t lo_neg, uint32_t hi_neg) -> uint32_t {
-        return 0x3F803F80u | ((lo_neg & 1u) << 15) | ((hi_neg & 1u) << 31);
-    };
-    // H64 as the A operand of the second product: row 16 ot + c, k-slot e as
-    // above.  (-1)^popcount of (c & e & 3), ((c >> 2) & g), (ot & 1 & e >> 2)
-    // and (ot >> 1 & st).
-    const uint32_t pl = __builtin_popcount((c >> 2) & g) & 1;
-    const uint32_t q1 = c & 1, q2 = (c >> 1) & 1, q3 = __builtin_popcount(c & 3) & 1;
-    const uint32_t hbase0 = pm1(pl, q1 ^ pl), hbase1 = pm1(q2 ^ pl, q3 ^ pl);
-    // H64 as the B operand of the first product: column 16 jt + c, k-slot e
-    // -> row 32 ks + 8 g + e.  (-1)^popcount of (e & c & 7), ((g & 1) &
-    // (c >> 3)), ((g >> 1) & jt & 1) and (ks & jt >> 1).
-    const uint32_t pb = (g & 1) & (c >> 3);
-    bf16x8_t hb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t f = ((((g >> 1) & jt) ^ (ks & (jt >> 1))) & 1) ? 0x80008000u : 0u;
-        u32x4_t v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            v[q] = pm1((__builtin_popcount((2 * q) & c & 7) & 1) ^ pb,
-                       (__builtin_popcount((2 * q + 1) & c & 7) & 1) ^ pb) ^ f;
-        hb[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-    // Z; lane holds Z[16 it + 4 g + r][16 jt + c].  A operand: X[16 it + c][32 ks + 8 g + 0..7]
-    f32x4_t z[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        z[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int at = (16 * it + c) * kPadX + 32 * ks + 8 * g;
-            if constexpr (!IN_F32) {
-                const u32x4_t xa = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(xs) + at);
-                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), hb[ks], z[it], 0, 0, 0);
-            } else {
-                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint32_t *>(xs) + at);
-                const u32x4_t w0 = src[0], w1 = src[1];
-                u32x4_t xh, xl;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float f0 = __builtin_bit_cast(float, v < 2 ? w0[2 * v] : w1[2 * v - 4]);
-                    const float f1 = __builtin_bit_cast(float, v < 2 ? w0[2 * v + 1] : w1[2 * v - 3]);
-                    const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
-                    const bf16x2_t plo = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
-                    xh[v] = __builtin_bit_cast(uint32_t, ph);
-                    xl[v] = __builtin_bit_cast(uint32_t, plo);
-                }
-                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xh), hb[ks], z[it], 0, 0, 0);
-                z[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xl), hb[ks], z[it], 0, 0, 0);
-            }
-        }
-    }
-    // Z as three bfloat16 parts, in the k-slot order of the second product:
-    // slots 2v, 2v + 1 of step st are tile 2 st + (v >> 1), rows 2 (v & 1), + 1
-    u32x4_t zp[3][2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float f0 = z[2 * st + (v >> 1)][2 * (v & 1)];
-            float f1 = z[2 * st + (v >> 1)][2 * (v & 1) + 1];
-#pragma unroll
-            for (int pt = 0; pt < 3; ++pt) {
-                const bf16x2_t b = {(__bf16)f0, (__bf16)f1};
-                zp[pt][st][v] = __builtin_bit_cast(uint32_t, b);
-                f0 -= (float)b[0];
-                f1 -= (float)b[1];
-            }
-        }
-    // X' = H64 Z
-#pragma unroll
-    for (int ot = 0; ot < 4; ++ot) {
-        out[ot] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const uint32_t fa = ((ot >> 1) & st) ? 0x80008000u : 0u;  // every slot
-            const uint32_t fb = fa ^ ((ot & 1) ? 0x80008000u : 0u);   // slots e >= 4
-            const bf16x8_t ha = __builtin_bit_cast(bf16x8_t, u32x4_t{hbase0 ^ fa, hbase1 ^ fa, hbase0 ^ fb, hbase1 ^ fb});
-#pragma unroll
-            for (int pt = 0; pt < 3; ++pt)
-                out[ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, __builtin_bit_cast(bf16x8_t, zp[pt][st]), out[ot], 0, 0, 0);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // GEMV for M <= 16
 // ---------------------------------------------------------------------------
@@ -224,8 +119,25 @@ __device__ __forceinline__ void h64_slice(const void *xs, int jt, int c, int g, 
 
 // Eight consecutive binary32 activations (one MFMA A operand's worth).
 struct F32x8 {
-    u32x4_t v[2];
+    float e[8];
 };
+
+// Eight consecutive binary32 values from global memory (two 16-byte loads).
+__device__ __forceinline__ F32x8 load_f32x8(const float *src)
+{
+    const u32x4_t a = reinterpret_cast<const u32x4_t *>(src)[0];
+    const u32x4_t b = reinterpret_cast<const u32x4_t *>(src)[1];
+    F32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // copy the element out first: bit-casting an ext_vector element
+        // subscripted by a loop index reads element 0 (clang, this ROCm)
+        const unsigned ai = a[i], bi = b[i];
+        r.e[i] = __builtin_bit_cast(float, ai);
+        r.e[4 + i] = __builtin_bit_cast(float, bi);
+    }
+    return r;
+}
 
 // The bfloat16 part of eight binary32 values that one A row carries: the
 // rounding of each value (lo == false) or the rounding of its remainder
@@ -237,11 +149,16 @@ __device__ __forceinline__ bf16x8_t split_part(const F32x8 &f, bool lo)
     u32x4_t out;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const float f0 = __builtin_bit_cast(float, f.v[v >> 1][2 * (v & 1)]);
-        const float f1 = __builtin_bit_cast(float, f.v[v >> 1][2 * (v & 1) + 1]);
-        const bf16x2_t ph = {(__bf16)f0, (__bf16)f1};
-        const bf16x2_t pl = {(__bf16)(f0 - (float)ph[0]), (__bf16)(f1 - (float)ph[1])};
-        out[v] = lo ? __builtin_bit_cast(uint32_t, pl) : __builtin_bit_cast(uint32_t, ph);
+        float f0 = f.e[2 * v];
+        float f1 = f.e[2 * v + 1];
+        // the remainder rows round x - bf16(x) instead of x (a choice per
+        // value before the one pack of the pair)
+        if (lo) {
+            f0 -= (float)(__bf16)f0;
+            f1 -= (float)(__bf16)f1;
+        }
+        const bf16x2_t p = {(__bf16)f0, (__bf16)f1};
+        out[v] = __builtin_bit_cast(uint32_t, p);
     }
     return __builtin_bit_cast(bf16x8_t, out);
 }
@@ -719,12 +636,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 #pragma unroll
             for (int mu = 0; mu < 4; ++mu) {
                 if constexpr (XF32) {
-                    const u32x4_t *s0 = reinterpret_cast<const u32x4_t *>(xrow_f + 128 * gl0 + 8 * mu);
-                    const u32x4_t *s1 = reinterpret_cast<const u32x4_t *>(xrow_f + 128 * gl1 + 8 * mu);
-                    ag[slot][mu].v[0] = s0[0];
-                    ag[slot][mu].v[1] = s0[1];
-                    ag[slot][4 + mu].v[0] = s1[0];
-                    ag[slot][4 + mu].v[1] = s1[1];
+                    ag[slot][mu] = load_f32x8(xrow_f + 128 * gl0 + 8 * mu);
+                    ag[slot][4 + mu] = load_f32x8(xrow_f + 128 * gl1 + 8 * mu);
                 } else {
                     ag[slot][mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl0 + 8 * mu);
                     ag[slot][4 + mu] = *reinterpret_cast<const bf16x8_t *>(xrow + 128 * gl1 + 8 * mu);
@@ -1285,6 +1198,9 @@ const char *hip_error_string(int err) { return hipGetErrorString((hipError_t)err
 int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *codes,
                 const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream)
 {
+    // up to four rows: fp4 weights on the fp8 x fp4 matrix cores
+    if (f4_supported(M, N, K, false, x_f32))
+        return launch_gemv_f4(x, x_f32, nullptr, false, M, K, codes, scales, N, y, y_bf16, stream);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int step = gemv_rows_per_launch(N, K, x_f32);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
@@ -1353,10 +1269,20 @@ static int launch_rotate_rows(const void *x, bool x_f32, const int8_t *signs, in
     }
 }
 
+bool rotate_gemv_fits(int64_t M, int64_t N, int64_t K, int64_t block, bool x_f32)
+{
+    if (block == 4096 && f4_supported(M, N, K, true, x_f32)) return true;
+    return rotate_gemv_lds(M, N, K) <= kMaxLds;
+}
+
 int launch_rotate_gemv(const void *x, bool x_f32, const int8_t *signs, int block, int M, int64_t K,
                        const uint32_t *codes, const uint16_t *scales, int64_t N, void *y, bool y_bf16,
                        void *stream)
 {
+    // 4096-point blocks, up to four rows: the fp8 x fp4 kernel with the
+    // transform in its prologue
+    if (block == 4096 && f4_supported(M, N, K, true, x_f32))
+        return launch_gemv_f4(x, x_f32, signs, true, M, K, codes, scales, N, y, y_bf16, stream);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += kRotRowsPerLaunch) {
