@@ -11,15 +11,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtern.so")
 BENCH_LIB = os.path.join(HERE, "libtern_bench.so")  # measurement helper, not the matmul path
 
-# (source, extra flags).  The GEMM and the fp8 x fp4 GEMV keep their MFMA
-# results in ordinary VGPRs: both combine them with VALU arithmetic right
-# away (the GEMM's per-group rescale, the GEMV's part sums), and results in
-# accumulator registers would need a copy out for each.
+# (source, extra flags).  The GEMM keeps its MFMA results in ordinary VGPRs:
+# it rescales them with VALU arithmetic right away (per group), and results
+# in accumulator registers would need a copy out for each.
 SOURCES = [
     ("tern_kernels.hip", []),
     ("tern_gemm.hip", ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]),
     ("tern_t5.hip", []),
-    ("tern_f4.hip", ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]),
     ("tern_api.cpp", []),
     ("tern_codec.cpp", []),
 ]

@@ -34,12 +34,6 @@ int64_t gemm_max_k();
 int launch_gemv_t5(const void *x, int M, int64_t K, const uint8_t *data, const uint16_t *scales, int64_t N,
                    void *y, bool y_bf16, void *stream);
 int64_t t5_row_bytes(int64_t K);
-// fp8 x fp4 decode GEMV (tern_f4.hip): M <= 4; rot = signed 4096-point
-// rotation of x first (K a multiple of 4096).  f4_supported says whether the
-// shape fits one workgroup's LDS.
-bool f4_supported(int64_t M, int64_t N, int64_t K, bool rot, bool x_f32);
-int launch_gemv_f4(const void *x, bool x_f32, const int8_t *signs, bool rot, int M, int64_t K,
-                   const uint32_t *codes, const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream);
 // whether tern_rotate_gemv can run this shape in one pass over the weights
 bool rotate_gemv_fits(int64_t M, int64_t N, int64_t K, int64_t block, bool x_f32);
 

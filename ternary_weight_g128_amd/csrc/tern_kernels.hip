@@ -1198,9 +1198,6 @@ const char *hip_error_string(int err) { return hipGetErrorString((hipError_t)err
 int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *codes,
                 const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream)
 {
-    // up to four rows: fp4 weights on the fp8 x fp4 matrix cores
-    if (f4_supported(M, N, K, false, x_f32))
-        return launch_gemv_f4(x, x_f32, nullptr, false, M, K, codes, scales, N, y, y_bf16, stream);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int step = gemv_rows_per_launch(N, K, x_f32);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
@@ -1271,7 +1268,6 @@ static int launch_rotate_rows(const void *x, bool x_f32, const int8_t *signs, in
 
 bool rotate_gemv_fits(int64_t M, int64_t N, int64_t K, int64_t block, bool x_f32)
 {
-    if (block == 4096 && f4_supported(M, N, K, true, x_f32)) return true;
     return rotate_gemv_lds(M, N, K) <= kMaxLds;
 }
 
@@ -1279,10 +1275,6 @@ int launch_rotate_gemv(const void *x, bool x_f32, const int8_t *signs, int block
                        const uint32_t *codes, const uint16_t *scales, int64_t N, void *y, bool y_bf16,
                        void *stream)
 {
-    // 4096-point blocks, up to four rows: the fp8 x fp4 kernel with the
-    // transform in its prologue
-    if (block == 4096 && f4_supported(M, N, K, true, x_f32))
-        return launch_gemv_f4(x, x_f32, signs, true, M, K, codes, scales, N, y, y_bf16, stream);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += kRotRowsPerLaunch) {
