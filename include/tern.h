@@ -315,6 +315,26 @@ tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K,
                       const uint32_t *codes, const uint16_t *scales, int64_t N,
                       float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device scratch that tern_gemm_noalloc holds per device. */
+#define TERN_GEMM_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* tern_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * kernels and result as tern_gemm (bit for bit), with the partial sums of
+ * K-split tiles in a static device array of the library instead of a
+ * workspace argument: TERN_GEMM_SCRATCH_BYTES per device, held from the first
+ * call on that device until the process ends.  The call allocates nothing.
+ * The array's contents on entry do not matter (every partial sum is written
+ * before it is read).  All calls on one device share the array: calls that
+ * may overlap on one device (different streams, or host threads without an
+ * order between them) race and give wrong results; calls ordered on one
+ * stream are safe.  Arguments as tern_gemm, without the workspace.
+ * Errors: as tern_gemm; TERN_EUNSUPPORTED when tern_gemm_workspace_bytes(M,
+ * N, K) exceeds TERN_GEMM_SCRATCH_BYTES (use tern_gemm with a workspace). */
+tern_status tern_gemm_noalloc(const void *x, int xdt, int64_t M, int64_t K,
+                              const uint32_t *codes, const uint16_t *scales, int64_t N,
+                              float *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

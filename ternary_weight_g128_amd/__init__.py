@@ -23,6 +23,7 @@ TERN_MAX_K = 2147483520
 TERN_GROUP = 128
 TERN_GEMV_MAX_M = 16
 TERN_FWHT_MAX_BLOCK = 4096
+TERN_GEMM_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = [
     "tern_abi_version", "tern_status_str", "tern_last_error", "tern_codes_bytes",
@@ -31,7 +32,7 @@ EXPORTED = [
     "tern_gemm", "tern_scales_g64_bytes", "tern_scales_to_g64", "tern_scales_from_g64",
     "tern_mlx_export", "tern_mlx_import", "tern_b1_bytes", "tern_pack_b1", "tern_unpack_b1",
     "tern_b1_to_codes", "tern_codes_to_b1", "tern_mlx_export_b1", "tern_mlx_import_b1",
-    "tern_t5_bytes", "tern_pack_t5", "tern_unpack_t5", "tern_gemv_t5",
+    "tern_t5_bytes", "tern_pack_t5", "tern_unpack_t5", "tern_gemv_t5", "tern_gemm_noalloc",
 ]
 _SIZE_FNS = ("tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes",
              "tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes")
@@ -64,6 +65,7 @@ _lib.tern_rotate_gemv.argtypes = [_P, _I, _P, _I64, _I64, _I64, _P, _P, _I64, _P
 _lib.tern_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 _lib.tern_gemm_workspace_bytes.restype = _SZ
 _lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
+_lib.tern_gemm_noalloc.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P]
 _lib.tern_gemv_t5.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
 for _name in ("tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes"):
     getattr(_lib, _name).argtypes = [_I64, _I64]
@@ -472,6 +474,18 @@ def tern_gemm(x, codes, scales, out=None, workspace=None, stream=None):
     _check(_lib.tern_gemm(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
                           _dev_ptr(out), _dev_ptr(workspace), ws_bytes, _stream_ptr(stream)),
            "tern_gemm")
+    return out
+
+
+def tern_gemm_noalloc(x, codes, scales, out, stream=None):
+    """tern_gemm with the library's static device scratch instead of a
+    workspace: allocates nothing (the caller passes `out`)."""
+    M, K = _dims2("tern_gemm_noalloc", x)
+    N = codes.shape[0]
+    _matrix_shapes("tern_gemm_noalloc", x, K, codes, scales, out, M, N, out_sizes=(4,))
+    _check(_lib.tern_gemm_noalloc(_dev_ptr(x), _dt(x), M, K, _dev_ptr(codes), _dev_ptr(scales), N,
+                                  _dev_ptr(out), _stream_ptr(stream)),
+           "tern_gemm_noalloc")
     return out
 
 

@@ -142,29 +142,42 @@ size_t tern_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return tern::gemm_workspace_bytes(M, N, K);
 }
 
-tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *codes,
-                      const uint16_t *scales, int64_t N, float *y, void *workspace,
-                      size_t workspace_bytes, void *stream)
+namespace {
+
+// Checks shared by tern_gemm and tern_gemm_noalloc (all but the workspace).
+tern_status check_gemm_args(const char *fn, const void *x, int xdt, int64_t M, int64_t K,
+                            const uint32_t *codes, const uint16_t *scales, int64_t N, const float *y)
 {
-    tern_status st = check_matmul_args("tern_gemm", x, xdt, M, K, codes, scales, N, y);
+    tern_status st = check_matmul_args(fn, x, xdt, M, K, codes, scales, N, y);
     if (st != TERN_OK) return st;
     if (xdt != TERN_BF16) {
-        set_error("tern_gemm: activations must be TERN_BF16");
+        set_error(std::string(fn) + ": activations must be TERN_BF16");
         return TERN_EUNSUPPORTED;
     }
     if (K > tern::gemm_max_k()) {
-        set_error("tern_gemm: K above " + std::to_string(tern::gemm_max_k()));
+        set_error(std::string(fn) + ": K above " + std::to_string(tern::gemm_max_k()));
         return TERN_EINVAL;
     }
     if (M == 0 || N == 0) return TERN_OK;
     if (!aligned(y, 4)) {
-        set_error("tern_gemm: y must be 4-byte aligned");
+        set_error(std::string(fn) + ": y must be 4-byte aligned");
         return TERN_EINVAL;
     }
     if (M > ((int64_t)1 << 31) - 256 || N > ((int64_t)1 << 31) - 256) {
-        set_error("tern_gemm: M or N too large");
+        set_error(std::string(fn) + ": M or N too large");
         return TERN_EINVAL;
     }
+    return TERN_OK;
+}
+
+}  // namespace
+
+tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *codes,
+                      const uint16_t *scales, int64_t N, float *y, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    tern_status st = check_gemm_args("tern_gemm", x, xdt, M, K, codes, scales, N, y);
+    if (st != TERN_OK || M == 0 || N == 0) return st;
     const size_t need = tern::gemm_workspace_bytes(M, N, K);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))) {
         set_error("tern_gemm: workspace missing, misaligned or smaller than "
@@ -174,6 +187,21 @@ tern_status tern_gemm(const void *x, int xdt, int64_t M, int64_t K, const uint32
     return device_status(
         tern::launch_gemm(x, M, K, codes, scales, N, y, workspace, workspace_bytes, stream),
         "tern_gemm");
+}
+
+tern_status tern_gemm_noalloc(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *codes,
+                              const uint16_t *scales, int64_t N, float *y, void *stream)
+{
+    tern_status st = check_gemm_args("tern_gemm_noalloc", x, xdt, M, K, codes, scales, N, y);
+    if (st != TERN_OK || M == 0 || N == 0) return st;
+    const size_t need = tern::gemm_workspace_bytes(M, N, K);
+    if (need > TERN_GEMM_SCRATCH_BYTES) {
+        set_error("tern_gemm_noalloc: these sizes need " + std::to_string(need) +
+                  " bytes of scratch, above TERN_GEMM_SCRATCH_BYTES = " +
+                  std::to_string((size_t)TERN_GEMM_SCRATCH_BYTES) + "; use tern_gemm with a workspace");
+        return TERN_EUNSUPPORTED;
+    }
+    return device_status(tern::launch_gemm_noalloc(x, M, K, codes, scales, N, y, stream), "tern_gemm_noalloc");
 }
 
 tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uint8_t *data,

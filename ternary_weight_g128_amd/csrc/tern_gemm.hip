@@ -432,6 +432,47 @@ bool gemm_splits_tiles(const GemmArgs &a) { return a.items > 0; }
 
 }  // namespace
 
+// Scratch of the allocation-free entry point: the partial sums of K-split
+// tiles.  Every device holds its own instance until the process ends.  In
+// host code the array's name is not a device address: its address on each
+// device comes from hipGetSymbolAddress (gemm_scratch below).
+static __device__ __align__(256) unsigned char scratch[TERN_GEMM_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int gemm_scratch(void *stream, void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return (int)e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return (int)e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return (int)e;
+        if (p == nullptr) return (int)hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
+}
+
+}  // namespace
+
 namespace tern {
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -469,6 +510,18 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
     hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)(a.items / a.split), kGemmTileElems / 256), dim3(256),
                        0, st, a);
     return (int)hipGetLastError();
+}
+
+int launch_gemm_noalloc(const void *x, int64_t M, int64_t K, const uint32_t *codes, const uint16_t *scales,
+                        int64_t N, float *y, void *stream)
+{
+    const size_t need = gemm_workspace_bytes(M, N, K);
+    void *ws = nullptr;
+    if (need > 0) {
+        int rc = gemm_scratch(stream, &ws);
+        if (rc) return rc;
+    }
+    return launch_gemm(x, M, K, codes, scales, N, y, ws, need, stream);
 }
 
 }  // namespace tern

@@ -29,6 +29,10 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes,
                 const uint16_t *scales, int64_t N, float *y, void *workspace,
                 size_t workspace_bytes, void *stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// tern_gemm with its K-split partial sums in the library's static device
+// scratch (tern_gemm.hip); the caller has checked that they fit.
+int launch_gemm_noalloc(const void *x, int64_t M, int64_t K, const uint32_t *codes,
+                        const uint16_t *scales, int64_t N, float *y, void *stream);
 int launch_pack_device(const int8_t *t, int64_t N, int64_t K, uint32_t *codes, void *stream);
 int64_t gemm_max_k();
 int launch_gemv_t5(const void *x, int M, int64_t K, const uint8_t *data, const uint16_t *scales, int64_t N,

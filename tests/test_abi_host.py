@@ -114,6 +114,30 @@ def test_gemm_empty_is_noop(tern):
     assert _gemm(tern, M=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
 
 
+def _gemm_noalloc(tern, x=A16, xdt=1, M=64, K=128, codes=A16, scales=A16, N=16, y=A16):
+    return tern.lib().tern_gemm_noalloc(x, xdt, M, K, codes, scales, N, y, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=0), 4), (dict(xdt=3), 4), (dict(K=64), 1), (dict(M=-2), 1), (dict(K=1 << 31), 1),
+    (dict(x=NULL), 1), (dict(y=A2), 1), (dict(codes=A2), 1),
+])
+def test_gemm_noalloc_rejects(tern, kw, status):
+    # the same host checks as tern_gemm, before any device call
+    assert _gemm_noalloc(tern, **kw) == status
+
+
+def test_gemm_noalloc_empty_is_noop(tern):
+    assert _gemm_noalloc(tern, M=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
+    assert _gemm_noalloc(tern, N=0, x=NULL, codes=NULL, scales=NULL, y=NULL) == 0
+
+
+def test_gemm_scratch_constant_matches_header(tern):
+    src = open(os.path.join(ROOT, "include", "tern.h")).read()
+    m = re.search(r"#define TERN_GEMM_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tern.TERN_GEMM_SCRATCH_BYTES
+
+
 def _fwht(tern, x=A16, xdt=0, signs=NULL, M=1, K=4096, block=4096, inverse=0, y=A16):
     return tern.lib().tern_fwht(x, xdt, signs, M, K, block, inverse, y, NULL)
 
