@@ -75,6 +75,22 @@ def sampled_rows(N: int, count: int, seed: int) -> np.ndarray:
     return np.array(sorted(picks), dtype=np.int64)
 
 
+def oracle_threads(oracle_lib) -> int:
+    """Host threads for the threaded oracle (bit-identical to one thread);
+    at most 16, the host share of one GPU."""
+    return max(1, min(16, oracle_lib.max_threads()))
+
+
+def full_problem(tern, seed: int, N: int, K: int, p_zero: float):
+    """A whole seeded matrix on the device and on the host (int8 t and the
+    binary16 scale bits), for every-element comparisons.  The same stream
+    as big_problem."""
+    t = synth.ternary(seed, N, K, p_zero)
+    s = synth.scales_f16(seed, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    return codes_d, scales_d, t, s
+
+
 def big_problem(tern, seed: int, N: int, K: int, p_zero: float, rows: np.ndarray):
     """Pack a large seeded matrix chunk by chunk straight to device memory,
     keeping the int8 rows `rows` for the oracle.  Returns (codes_dev,

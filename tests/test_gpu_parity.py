@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import synth
-from tests._helpers import (assert_fwht_close, assert_matmul_close, big_problem, pack_to_device,
-                            sampled_rows, torch, x_to_device, y_to_host)
+from tests._helpers import (assert_fwht_close, assert_matmul_close, big_problem, full_problem,
+                            oracle_threads, pack_to_device, sampled_rows, torch, x_to_device, y_to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,22 +190,21 @@ def test_gemv_k_zero_gives_zeros(tern):
 
 
 # Full sizes of the decode workloads, in the launch configuration the
-# benchmark uses, checked on sampled output rows (all M for each row).
+# benchmark uses: every output element against the (threaded) oracle.
 FULL = [(1, 1024, 1024, "f32", 1 / 3), (1, 4096, 12288, "f32", 0.35)] + \
        [(m, k, n, "bf16", 1 / 3) for m in (1, 2, 4, 8, 16) for (k, n) in ((5120, 17408), (17408, 5120))] + \
        [(1, 5120, 12288, "bf16", 1 / 3), (1, 6144, 5120, "bf16", 1 / 3)]
 
 
 @pytest.mark.parametrize("M,K,N,xdt,p0", FULL)
-def test_gemv_full_size_sampled(tern, oracle_lib, M, K, N, xdt, p0):
+def test_gemv_full_size_every_element(tern, oracle_lib, M, K, N, xdt, p0):
     seed = 1000 + K + N + M
     print(f"full gemv M={M} K={K} N={N} seed={seed}", flush=True)
-    rows = sampled_rows(N, 160, seed)
-    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, N, K, p0, rows)
+    codes_d, scales_d, t, s = full_problem(tern, seed, N, K, p0)
     x = _x(seed, M, K, xdt)
     y = _run_gemv(tern, x, codes_d, scales_d)
-    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t_rows), s_rows, K)
-    assert_matmul_close(y[:, rows], y_ref, bound, what=f"full M{M} K{K} N{N}")
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y, y_ref, bound, what=f"full M{M} K{K} N{N}")
 
 
 def test_gemv_lm_head_size_sampled(tern, oracle_lib):
@@ -271,11 +270,11 @@ def test_fwht_closed_forms(tern):
 # ---------------------------------------------------------------------------
 
 def test_rotated_decode_full_size(tern, oracle_lib):
+    """Two-launch rotated decode at its full size, every output element."""
     w = synth.ROTATED
     seed = 2024
     print("rotated decode", flush=True)
-    rows = sampled_rows(w.N, 200, seed)
-    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, w.N, w.K, w.p_zero, rows)
+    codes_d, scales_d, t, s = full_problem(tern, seed, w.N, w.K, w.p_zero)
     x = synth.activations_bf16(seed, w.M, w.K)
     d = synth.signs(seed, w.K)
     T = torch()
@@ -286,17 +285,17 @@ def test_rotated_decode_full_size(tern, oracle_lib):
     xr_ref = oracle_lib.fwht(oracle_lib.bf16_bits_to_f64(x), d, w.rotate_block)
     assert_fwht_close(xr_h, xr_ref, what="rotation")
     # the GEMV on the rotation it was given ...
-    codes_o = oracle_lib.encode(t_rows)
-    y_ref, bound = oracle_lib.matmul(xr_h.astype(np.float32), codes_o, s_rows, w.K)
-    assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound, what="gemv on rotated x")
+    codes_o = oracle_lib.encode(t)
+    nt = oracle_threads(oracle_lib)
+    y_ref, bound = oracle_lib.matmul(xr_h.astype(np.float32), codes_o, s, w.K, threads=nt)
+    assert_matmul_close(y_to_host(y), y_ref, bound, what="gemv on rotated x")
     # ... and end to end against the FP64 rotation (its own error adds
-    # sum |s t| * |dx| <= sum |s t| * 1e-5 * ||x'|| per output)
-    y64, b64 = oracle_lib.matmul(xr_ref, codes_o, s_rows, w.K)
+    # sum |s t| * |dx| per output)
+    y64, b64 = oracle_lib.matmul(xr_ref, codes_o, s, w.K, threads=nt)
     dx = np.abs(xr_h - xr_ref)
-    wabs = np.abs(oracle_lib.dequant(codes_o, s_rows, w.K))
+    wabs = np.abs(oracle_lib.dequant(codes_o, s, w.K))
     # allowance 1e-4 * B + sum |s t| |dx|, expressed through the bound
-    assert_matmul_close(y_to_host(y)[:, rows], y64, b64 + 1e4 * (dx @ wabs.T),
-                        what="rotated decode end to end")
+    assert_matmul_close(y_to_host(y), y64, b64 + 1e4 * (dx @ wabs.T), what="rotated decode end to end")
 
 
 # ---------------------------------------------------------------------------
@@ -335,11 +334,12 @@ def test_rotate_gemv_matches_oracle(tern, oracle_lib, M, K, N, block, xdt, signe
 
 
 def test_rotate_gemv_full_size_matches_two_launch_path(tern, oracle_lib):
+    """Fused rotated decode (one launch) at its full size, every output
+    element, beside the two-launch path."""
     w = synth.ROTATED
     seed = 606
     print("rotated decode fused", flush=True)
-    rows = sampled_rows(w.N, 200, seed)
-    codes_d, scales_d, t_rows, s_rows = big_problem(tern, seed, w.N, w.K, w.p_zero, rows)
+    codes_d, scales_d, t, s = full_problem(tern, seed, w.N, w.K, w.p_zero)
     T = torch()
     x = synth.activations_bf16(seed, 1, w.K)
     d = synth.signs(seed, w.K)
@@ -350,12 +350,12 @@ def test_rotate_gemv_full_size_matches_two_launch_path(tern, oracle_lib):
     T.cuda.synchronize()
     assert T.equal(y1, y1b)                      # deterministic
     xr = oracle_lib.fwht(oracle_lib.bf16_bits_to_f64(x), d, w.rotate_block)
-    codes_o = oracle_lib.encode(t_rows)
-    y_ref, bound = oracle_lib.matmul(xr, codes_o, s_rows, w.K)
-    wabs = np.abs(oracle_lib.dequant(codes_o, s_rows, w.K))
+    codes_o = oracle_lib.encode(t)
+    y_ref, bound = oracle_lib.matmul(xr, codes_o, s, w.K, threads=oracle_threads(oracle_lib))
+    wabs = np.abs(oracle_lib.dequant(codes_o, s, w.K))
     rot_err = 1e-5 * np.linalg.norm(xr) * np.sqrt((wabs ** 2).sum(axis=1))[None, :]
     for y in (y1, y2):
-        assert_matmul_close(y_to_host(y)[:, rows], y_ref, bound + 1e4 * rot_err, what="fused vs oracle")
+        assert_matmul_close(y_to_host(y), y_ref, bound + 1e4 * rot_err, what="fused vs oracle")
 
 
 # ---------------------------------------------------------------------------
