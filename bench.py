@@ -577,10 +577,12 @@ def bench_prefill(tern, torch, synth, steps):
 
 
 def bench_chain(tern, torch, synth, passes=5):
-    """The 27B-class decode weight pass: 64 blocks of five chained GEMVs plus
-    the LM head (321 dependent launches), M=1, bf16 activations.  Where the
-    lengths match, a link's output (bf16) is the next link's input; the
-    6144-wide input of each block's second link is a fixed seeded vector.
+    """The 27B-class decode weight pass: 64 blocks of four chained GEMVs
+    (gate and up as one matrix of both, since they take the same input) plus
+    the LM head (257 dependent launches), M=1, bf16 activations.  Where the
+    lengths match, a link's output (bf16) is the next link's input (the down
+    projection takes the up half of the gate/up output); the 6144-wide input
+    of each block's second link is a fixed seeded vector.
     Weights are drawn and packed on the GPU (6.49 GB resident).  `passes`
     full passes are captured in one HIP graph and timed, and timed again as
     plain launches on the stream."""
@@ -600,20 +602,20 @@ def bench_chain(tern, torch, synth, passes=5):
     cur = torch.empty((1, 5120), dtype=torch.bfloat16, device="cuda")
     h5120 = torch.empty((1, 5120), dtype=torch.bfloat16, device="cuda")
     qkv = torch.empty((1, 12288), dtype=torch.bfloat16, device="cuda")
-    gate = torch.empty((1, 17408), dtype=torch.bfloat16, device="cuda")
-    up = torch.empty((1, 17408), dtype=torch.bfloat16, device="cuda")
+    gate_up = torch.empty((1, 2 * synth.CHAIN_GATE_UP), dtype=torch.bfloat16, device="cuda")
+    up = gate_up[:, synth.CHAIN_GATE_UP:]
     logits = torch.empty((1, synth.LM_HEAD[1]), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
     def one_pass(_i):
         cur.copy_(x5120)
+        nl = len(synth.CHAIN_BLOCK)
         for b in range(synth.CHAIN_BLOCKS):
-            w = weights[5 * b: 5 * b + 5]
+            w = weights[nl * b: nl * b + nl]
             tern.tern_gemv(cur, *w[0], out=qkv)           # 5120 -> 12288
             tern.tern_gemv(x6144, *w[1], out=h5120)       # 6144 -> 5120 (fixed input)
-            tern.tern_gemv(h5120, *w[2], out=gate)        # 5120 -> 17408
-            tern.tern_gemv(h5120, *w[3], out=up)          # 5120 -> 17408
-            tern.tern_gemv(up, *w[4], out=cur)            # 17408 -> 5120
+            tern.tern_gemv(h5120, *w[2], out=gate_up)     # 5120 -> 17408 + 17408
+            tern.tern_gemv(up, *w[3], out=cur)            # 17408 -> 5120
         tern.tern_gemv(cur, *weights[-1], out=logits)     # LM head
 
     one_pass(0)

@@ -129,9 +129,12 @@ PREFILL = [Workload(f"prefill gemm M512 K{k} N{n}", 512, k, n, "bf16", p_zero=0.
                     outlier_frac=0.01) for (k, n) in ((5120, 17408), (17408, 5120))]
 
 # One decode step of a 64-block 27B-class stack: per block an attention-like
-# pair (5120->12288, 6144->5120), an MLP gate/up pair (5120->17408 twice) and a
-# down projection (17408->5120); then a 5120->248320 LM head.  (K, N) per link.
-CHAIN_BLOCK = [(5120, 12288), (6144, 5120), (5120, 17408), (5120, 17408), (17408, 5120)]
+# pair (5120->12288, 6144->5120), the MLP gate and up projections (5120->17408
+# each, the same input, stored as one 34816-row matrix: rows 0..17407 gate,
+# 17408..34815 up) and a down projection (17408->5120); then a 5120->248320
+# LM head.  (K, N) per link.
+CHAIN_GATE_UP = 17408
+CHAIN_BLOCK = [(5120, 12288), (6144, 5120), (5120, 2 * CHAIN_GATE_UP), (17408, 5120)]
 CHAIN_BLOCKS = 64
 LM_HEAD = (5120, 248320)
 

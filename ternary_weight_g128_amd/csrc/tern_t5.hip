@@ -25,10 +25,13 @@
 // group g = l >> 4: per superblock it loads bytes 16g..16g+15 of each
 // 64-byte half c of the row's 128 bytes, which hold weights i = 64c + 16g +
 // 0..15 of all the superblock's groups.  The eight bytes of operand half h
-// (i = 64c + 16g + 8h + 0..7) are split into the 16-bit halves of two
-// registers per dword (bytes 0, 2 and 1, 3), so the eight bfloat16 elements
-// of one MFMA B operand hold i offsets {0, 2, 1, 3, 4, 6, 5, 7}; the
-// activations are staged in LDS in that order.
+// (i = 64c + 16g + 8h + 0..7) go in consecutive pairs into the 16-bit halves
+// of four registers (one byte permute each), so the eight bfloat16 elements
+// of one MFMA B operand are weights i = 64c + 16g + 8h + 0..7 in order, and
+// the matching A operand is eight consecutive activations: a 16-byte chunk of
+// x, read from an LDS copy of x (up to four rows) or straight from memory
+// (more rows, where the copy would not fit or would be made by every
+// workgroup at a cost above the direct reads).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -47,6 +50,7 @@ typedef unsigned short u16x2v_t __attribute__((ext_vector_type(2)));
 
 constexpr int kT5Bytes = 128;       // bytes per superblock row segment
 constexpr int kT5Groups = 5;        // scale groups per superblock
+constexpr unsigned kBufRaw = 0x00020000u;  // raw buffer resource, 32-bit data format
 
 struct T5Args {
     const uint16_t *x;      // bfloat16 [M][K]
@@ -87,7 +91,7 @@ __device__ __forceinline__ int t5_seg(int sb, int c, int j, int h, int g, int m,
     return ((((sb * 2 + c) * kT5Groups + j) * 2 + h) * 4 + g) * mx + m;
 }
 
-template <int MX>
+template <int MX, bool AG>
 __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -101,50 +105,74 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
     const int sb_begin = (int)((int64_t)wave * a.SB / waves);
     const int sb_end = (int)((int64_t)(wave + 1) * a.SB / waves);
     u32x4_t *lds_x = reinterpret_cast<u32x4_t *>(smem);
-    float *red = reinterpret_cast<float *>(smem + (size_t)a.SB * 80 * MX * 16);
+    float *red = reinterpret_cast<float *>(smem + (AG ? 0 : (size_t)a.SB * 80 * MX * 16));
 
-    // code stream of this lane's row (rows past N read the last row; their
-    // results are dropped), one superblock ahead; the prefetch of the last
-    // superblock re-reads it, so that every load is unconditional
-    int64_t r = n0 + nn;
-    if (r > a.N - 1) r = a.N - 1;
-    const uint8_t *drow = a.data + r * ((int64_t)a.SB * kT5Bytes) + 16 * g;
-    const uint16_t *srow = a.scales + r * a.G;
+    // Code stream of this lane's row, one superblock ahead, by raw buffer
+    // loads over the tile's rows (rows past N read zeros; their results are
+    // dropped); the prefetch of the last superblock re-reads it, so that
+    // every load is unconditional.  Buffer loads also keep the compiler from
+    // merging the prefetch with the next iteration's use (it does so with
+    // plain loads that meet in a loop phi).
+    const int64_t rows_here = a.N - n0 < kTileN ? a.N - n0 : kTileN;
+    const int rowb = a.SB * kT5Bytes;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.data + n0 * rowb), (short)0, (int)(rows_here * rowb), (int)kBufRaw);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scales + n0 * a.G), (short)0, (int)(rows_here * a.G * 2), (int)kBufRaw);
+    const int cvo = nn * rowb + 16 * g, svo = nn * a.G * 2;
     const bool any = sb_begin < sb_end;
     u32x4_t cur0 = {0u, 0u, 0u, 0u}, cur1 = cur0;
     uint16_t csc[kT5Groups] = {0, 0, 0, 0, 0};
     auto load_sb = [&](int sb, u32x4_t &c0, u32x4_t &c1, uint16_t (&sh)[kT5Groups]) {
-        c0 = *reinterpret_cast<const u32x4_t *>(drow + (int64_t)sb * kT5Bytes);
-        c1 = *reinterpret_cast<const u32x4_t *>(drow + (int64_t)sb * kT5Bytes + 64);
+        c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, sb * kT5Bytes, 0));
+        c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, sb * kT5Bytes + 64, 0));
 #pragma unroll
         for (int j = 0; j < kT5Groups; ++j) {
             const int gi = kT5Groups * sb + j;
-            sh[j] = srow[gi < a.G ? gi : a.G - 1];
+            sh[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, 2 * (gi < a.G ? gi : a.G - 1), 0);
         }
     };
     if (any) load_sb(sb_begin, cur0, cur1, csc);
 
-    // stage the activations: unit = 8 consecutive k of one row (16 bytes);
-    // the groups a short last superblock lacks are staged as zeros, so that
-    // their (unused) products are exact zeros
-    const int upr = a.SB * 80;  // units per row, padded to whole superblocks
-    const int units = a.M * upr;
-    for (int u = threadIdx.x; u < units; u += blockDim.x) {
-        const int m = u / upr;
-        const int k = 8 * (u - m * upr);
-        const bool live = k < a.K;
-        u32x4_t d = *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)m * a.K + (live ? k : 0));
-        if (!live) d = u32x4_t{0u, 0u, 0u, 0u};
-        const int sb = k / 640, rem = k - 640 * sb;
-        const int j = rem >> 7, c = (rem >> 6) & 1, gg = (rem >> 4) & 3, h = (rem >> 3) & 1;
-        u32x4_t o;
-        o[0] = (d[0] & 0xffffu) | (d[1] << 16);          // k + 0, k + 2
-        o[1] = (d[0] >> 16) | (d[1] & 0xffff0000u);      // k + 1, k + 3
-        o[2] = (d[2] & 0xffffu) | (d[3] << 16);          // k + 4, k + 6
-        o[3] = (d[2] >> 16) | (d[3] & 0xffff0000u);      // k + 5, k + 7
-        lds_x[t5_seg(sb, c, j, h, gg, m, MX)] = o;
+    // A operands.  Staged: unit = 8 consecutive k of one row (16 bytes),
+    // copied into the LDS image; the groups a short last superblock lacks
+    // are staged as zeros, so that their (unused) products are exact zeros.
+    // Direct: each lane reads its own chunks (rows past M read row M - 1,
+    // whose results are dropped; a group past G re-reads group G - 1, whose
+    // products meet a zero scale), one superblock ahead like the codes.
+    u32x4_t xa[2][2][kT5Groups], xn[2][2][kT5Groups];
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.x, (short)0, (int)((int64_t)a.M * a.K * 2), (int)kBufRaw);
+    const int xvo = ((a_active ? nn : a.M - 1) * a.K + 16 * g) * 2;
+    auto load_a = [&](int sb, u32x4_t (&dst)[2][2][kT5Groups]) {
+#pragma unroll
+        for (int j = 0; j < kT5Groups; ++j) {
+            const int gi = kT5Groups * sb + j < a.G ? kT5Groups * sb + j : a.G - 1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    dst[c][h][j] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo, 2 * (kGroup * gi + 64 * c + 8 * h), 0));
+        }
+    };
+    if constexpr (AG) {
+        if (any) load_a(sb_begin, xa);
+    } else {
+        const int upr = a.SB * 80;  // units per row, padded to whole superblocks
+        const int units = a.M * upr;
+        for (int u = threadIdx.x; u < units; u += blockDim.x) {
+            const int m = u / upr;
+            const int k = 8 * (u - m * upr);
+            const bool live = k < a.K;
+            u32x4_t d = *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)m * a.K + (live ? k : 0));
+            if (!live) d = u32x4_t{0u, 0u, 0u, 0u};
+            const int sb = k / 640, rem = k - 640 * sb;
+            const int j = rem >> 7, c = (rem >> 6) & 1, gg = (rem >> 4) & 3, h = (rem >> 3) & 1;
+            lds_x[t5_seg(sb, c, j, h, gg, m, MX)] = d;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     float yacc[kRowsOut];
 #pragma unroll
@@ -156,6 +184,7 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
         u32x4_t nxt0, nxt1;
         uint16_t nsc[kT5Groups];
         load_sb(sb + 1 < sb_end ? sb + 1 : sb, nxt0, nxt1, nsc);
+        if constexpr (AG) load_a(sb + 1 < sb_end ? sb + 1 : sb, xn);
         f32x4_t acc[kT5Groups];
 #pragma unroll
         for (int j = 0; j < kT5Groups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -166,12 +195,19 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
             for (int h = 0; h < 2; ++h) {
                 u32x4_t xs[kT5Groups];
 #pragma unroll
-                for (int j = 0; j < kT5Groups; ++j)
-                    xs[j] = a_active ? lds_x[t5_seg(sb, c, j, h, g, nn, MX)] : zero4;
+                for (int j = 0; j < kT5Groups; ++j) {
+                    if constexpr (AG)
+                        xs[j] = xa[c][h][j];
+                    else
+                        xs[j] = a_active ? lds_x[t5_seg(sb, c, j, h, g, nn, MX)] : zero4;
+                }
                 unsigned f[4][kT5Groups];
                 const unsigned d0 = cw[2 * h], d1 = cw[2 * h + 1];
-                const unsigned pairs[4] = {d0 & 0x00ff00ffu, (d0 >> 8) & 0x00ff00ffu,   // bytes 0, 2 | 1, 3
-                                           d1 & 0x00ff00ffu, (d1 >> 8) & 0x00ff00ffu};  // bytes 4, 6 | 5, 7
+                // consecutive byte pairs into the 16-bit halves: bytes 0, 1 | 2, 3 | 4, 5 | 6, 7
+                const unsigned pairs[4] = {__builtin_amdgcn_perm(0u, d0, 0x0c010c00u),
+                                           __builtin_amdgcn_perm(0u, d0, 0x0c030c02u),
+                                           __builtin_amdgcn_perm(0u, d1, 0x0c010c00u),
+                                           __builtin_amdgcn_perm(0u, d1, 0x0c030c02u)};
                 t5_patterns(pairs, f);
 #pragma unroll
                 for (int j = 0; j < kT5Groups; ++j) {
@@ -189,6 +225,14 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
         }
         cur0 = nxt0;
         cur1 = nxt1;
+        if constexpr (AG) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < kT5Groups; ++j) xa[c][h][j] = xn[c][h][j];
+        }
 #pragma unroll
         for (int j = 0; j < kT5Groups; ++j) csc[j] = nsc[j];
     }
@@ -214,10 +258,10 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
     }
 }
 
-size_t t5_lds(int64_t K, int mx, int waves)
+size_t t5_lds(int64_t K, int mx, int waves, bool ag)
 {
     const int64_t SB = (K / kGroup + kT5Groups - 1) / kT5Groups;
-    return (size_t)SB * 80 * mx * 16 + (size_t)waves * mx * kTileN * sizeof(float);
+    return (ag ? 0 : (size_t)SB * 80 * mx * 16) + (size_t)waves * mx * kTileN * sizeof(float);
 }
 
 int t5_waves(int64_t K)
@@ -226,15 +270,21 @@ int t5_waves(int64_t K)
     return SB >= 4 ? 4 : (SB >= 1 ? (int)SB : 1);
 }
 
+// Direct A loads from five rows on (every workgroup would otherwise copy
+// 5..16 rows of x into LDS), or wherever the LDS copy would not fit.
+bool t5_direct(int64_t K, int mx) { return mx > 4 || t5_lds(K, mx, t5_waves(K), false) > kMaxLds; }
+
 template <int MX>
 int launch_t5_mx(const T5Args &a, hipStream_t stream)
 {
     const int waves = t5_waves(a.K);
-    const size_t lds = t5_lds(a.K, MX, waves);
-    int rc = ensure_lds(gemv_t5_kernel<MX>, lds);
+    const bool ag = t5_direct(a.K, MX);
+    const size_t lds = t5_lds(a.K, MX, waves, ag);
+    void (*kernel)(T5Args) = ag ? gemv_t5_kernel<MX, true> : gemv_t5_kernel<MX, false>;
+    int rc = ensure_lds(kernel, lds);
     if (rc) return rc;
     const unsigned wgs = (unsigned)((a.N + kTileN - 1) / kTileN);
-    hipLaunchKernelGGL(gemv_t5_kernel<MX>, dim3(wgs), dim3(64 * waves), lds, stream, a);
+    hipLaunchKernelGGL(kernel, dim3(wgs), dim3(64 * waves), lds, stream, a);
     return (int)hipGetLastError();
 }
 
@@ -244,43 +294,30 @@ namespace tern {
 
 int64_t t5_row_bytes(int64_t K) { return ((K / kGroup + kT5Groups - 1) / kT5Groups) * kT5Bytes; }
 
-// Rows of x one launch takes (the staged activations must fit in LDS).
-int t5_rows_per_launch(int64_t K)
-{
-    for (int rows = 16; rows > 1; rows /= 2)
-        if (t5_lds(K, rows, t5_waves(K)) <= kMaxLds) return rows;
-    return 1;
-}
-
 int launch_gemv_t5(const void *x, int M, int64_t K, const uint8_t *data, const uint16_t *scales, int64_t N,
                    void *y, bool y_bf16, void *stream)
 {
+    // one launch for every M <= 16: the weights are read once
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int per = t5_rows_per_launch(K);
-    for (int m0 = 0; m0 < M; m0 += per) {
-        T5Args a;
-        a.M = (M - m0) < per ? (M - m0) : per;
-        a.x = static_cast<const uint16_t *>(x) + (int64_t)m0 * K;
-        a.data = data;
-        a.scales = scales;
-        a.y = static_cast<char *>(y) + (size_t)m0 * N * (y_bf16 ? 2 : 4);
-        a.N = N;
-        a.K = (int)K;
-        a.G = (int)(K / kGroup);
-        a.SB = (int)((a.G + kT5Groups - 1) / kT5Groups);
-        a.y_bf16 = y_bf16 ? 1 : 0;
-        const int mx = a.M <= 1 ? 1 : a.M <= 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
-        int rc;
-        switch (mx) {
-        case 1: rc = launch_t5_mx<1>(a, st); break;
-        case 2: rc = launch_t5_mx<2>(a, st); break;
-        case 4: rc = launch_t5_mx<4>(a, st); break;
-        case 8: rc = launch_t5_mx<8>(a, st); break;
-        default: rc = launch_t5_mx<16>(a, st); break;
-        }
-        if (rc) return rc;
+    T5Args a;
+    a.M = M;
+    a.x = static_cast<const uint16_t *>(x);
+    a.data = data;
+    a.scales = scales;
+    a.y = y;
+    a.N = N;
+    a.K = (int)K;
+    a.G = (int)(K / kGroup);
+    a.SB = (int)((a.G + kT5Groups - 1) / kT5Groups);
+    a.y_bf16 = y_bf16 ? 1 : 0;
+    const int mx = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    switch (mx) {
+    case 1: return launch_t5_mx<1>(a, st);
+    case 2: return launch_t5_mx<2>(a, st);
+    case 4: return launch_t5_mx<4>(a, st);
+    case 8: return launch_t5_mx<8>(a, st);
+    default: return launch_t5_mx<16>(a, st);
     }
-    return 0;
 }
 
 }  // namespace tern

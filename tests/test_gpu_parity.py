@@ -525,9 +525,10 @@ def test_chained_block_links(tern, oracle_lib):
 
     run(0, x5120)              # 5120 -> 12288
     h = run(1, x6144)          # 6144 -> 5120
-    run(2, h)                  # 5120 -> 17408 (gate)
-    up = run(3, h)             # 5120 -> 17408 (up)
-    out = run(4, up)           # 17408 -> 5120 (down): the next block's input
+    gu = run(2, h)             # 5120 -> 17408 (gate) + 17408 (up), one matrix
+    up = gu[:, synth.CHAIN_GATE_UP:]
+    assert up.is_contiguous()
+    out = run(3, up)           # 17408 -> 5120 (down): the next block's input
     assert out.shape == (1, 5120) and T.isfinite(out.float()).all()
 
 
