@@ -58,7 +58,7 @@ def gemv_bytes(M, K, N, x_bytes):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_rotated_M1_K4096_N12288_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "ternary_weight_g128_amd", "csrc", f)
-                  for f in ("tern_kernels.hip", "tern_device.h")]
+                  for f in ("tern_kernels.hip", "tern_device.h", "tern_h64.h")]
 
 
 def measured_traffic():
