@@ -801,6 +801,265 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Decode GEMV with 5..16 bfloat16 rows: A operands through a shared LDS ring
+// ---------------------------------------------------------------------------
+//
+// From five A rows on, one 256-K block of activations (MX rows x 512 bytes)
+// outweighs the codes of a tile's block (1 KiB), so the number of tiles that
+// share one fetch of it sets the activation traffic.  A workgroup is WT
+// tile-waves x WK K-groups.  The WT waves of a K-group own different tiles
+// (TPW each) over the same K range and take their A operands from one LDS
+// ring of three 256-K blocks of x, which they fill together by buffer loads
+// to LDS two blocks ahead.  A block holds its MX rows in x's own order,
+// 32 16-byte chunks of 8 activations per row and one chunk of padding
+// (row stride 528 bytes), so that each load instruction (64 lanes, 1 KiB
+// of LDS) reads about two rows' contiguous 512 bytes, and the 16 rows of an
+// MFMA A operand (one 16-byte LDS read per lane: chunk 16 G + 4 {0, 2, 1,
+// 3}[g] + mu of its row, i.e. k = 128 G + 32 {0, 2, 1, 3}[g] + 8 mu + 0..7,
+// the order the permlane-regrouped code words give the B operand) fall on
+// 16 distinct bank groups.  One barrier per block publishes the block and
+// frees the slot read the block before.  Codes and scales stream per wave by raw buffer
+// loads, two blocks ahead (rows past N read zero; their outputs are
+// dropped).
+constexpr unsigned kBufRaw = 0x00020000u;  // raw buffer resource, 32-bit data format
+typedef __attribute__((address_space(3))) void lds_void_t;
+// s_waitcnt operand: vmcnt(n); expcnt and lgkmcnt not waited for
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// One 16-byte buffer load per lane straight into LDS (lane l writes dst +
+// 16 l).  A plain device function: with the builtin written inside a kernel
+// template, the host pass of this compiler drops the template's launch stub.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int MX, int TPW, int WT, bool SC4, int KD>
+__global__ __launch_bounds__(512) void gemv_ring_kernel(const GemvArgs a)
+{
+    constexpr int NS = 3;                             // ring slots (blocks of A)
+    constexpr int kRowSlots = 33;                     // 16-byte chunks per row: 32 and one of padding
+    constexpr int kLoads = ((MX * kRowSlots + 63) / 64 + WT - 1) / WT;  // loads to LDS per lane per block
+    constexpr int kChunk = kLoads * WT * 1024;        // LDS bytes of one block of A
+    constexpr int PF = 4;                             // code ring slots
+    constexpr int kDist = KD;                         // code blocks in flight (<= PF)
+    static_assert(KD >= 1 && KD <= PF, "the refill reuses a consumed slot");
+    constexpr int kCodeOps = TPW * (SC4 ? 2 : 3);     // loads per code refill
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wk = a.wk;
+    const int kg = wave / WT, tw = wave - kg * WT;
+    const int nn = lane & 15, g = lane >> 4;
+    const int G = a.K / kGroup;
+
+    const int b_begin = kg * a.bq + (kg < a.br ? kg : a.br);
+    const int nblocks = a.bq + (kg < a.br ? 1 : 0);
+    const int g_begin = 2 * b_begin;
+    const int g_end = (g_begin + 2 * nblocks < G) ? g_begin + 2 * nblocks : G;
+
+    const int rows_per_wg = kTileN * TPW * WT;
+    const int64_t n_wg = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t n0 = n_wg + (int64_t)tw * (kTileN * TPW);
+    unsigned char *ring = smem + (size_t)kg * NS * kChunk;
+    float *red = reinterpret_cast<float *>(smem + (size_t)wk * NS * kChunk);
+
+    // A chunks of this lane: slot p = (tw kLoads + q) 64 + lane of a block is
+    // chunk p % 33 of row p / 33.  Rows past M re-read row M - 1; padding
+    // slots and slots past the last row re-read a valid chunk (never read
+    // back); the second group of a one-group block (odd G) re-reads the
+    // first (its scale is zero).
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(a.x), (short)0, (int)((int64_t)a.M * a.K * 2), (int)kBufRaw);
+    int voff[kLoads], voff1[kLoads];
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int p = (tw * kLoads + q) * 64 + lane;
+        const int row = p / kRowSlots, c = p - row * kRowSlots;
+        const int r = row < a.M ? row : a.M - 1;
+        const int cc = c < 32 ? c : 0;
+        voff[q] = (r * a.K + 8 * cc) * 2;
+        voff1[q] = (r * a.K + 8 * (cc & 15)) * 2;
+    }
+    auto load_chunk = [&](int s, int slot) {
+        const int b = b_begin + (s < nblocks ? s : nblocks - 1);
+        const bool one = 2 * b + 1 >= G;
+        unsigned char *dst = ring + slot * kChunk + tw * kLoads * 1024;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q)
+            load_lds16(xrs, dst + 1024 * q, one ? voff1[q] : voff[q], 512 * b);
+    };
+
+    // code and scale streams of this wave's rows
+    const int64_t left = a.N - n0;
+    const int rows_here = left <= 0 ? 0 : (left < kTileN * TPW ? (int)left : kTileN * TPW);
+    const int row_bytes = a.K / 4;
+    const int64_t nb = rows_here > 0 ? n0 : 0;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.codes + nb * (a.K / 16)), (short)0, rows_here * row_bytes, (int)kBufRaw);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scales + nb * G), (short)0, rows_here * G * 2, (int)kBufRaw);
+    u32x4_t cbuf[PF][TPW];
+    uint32_t sbuf[PF][TPW];
+    // block b: words 4 g .. 4 g + 3 of its 256 K; a one-group block's upper
+    // lane groups re-read the first group
+    auto load_block = [&](int b, int p) {
+        b = b < nblocks ? b : nblocks - 1;
+        const int gb = g_begin + 2 * b;
+        const bool two = gb + 1 < g_end;
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            const int rowoff = (tp * kTileN + nn) * row_bytes;
+            cbuf[p][tp] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, rowoff + 16 * (two ? g : (g & 1)), 32 * gb, 0));
+            const int so = (tp * kTileN + nn) * G * 2;
+            if constexpr (SC4)
+                sbuf[p][tp] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 2 * gb, 0);
+            else
+                sbuf[p][tp] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(srs, so, 2 * gb, 0) |
+                              ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(srs, so, 2 * (two ? gb + 1 : gb), 0)
+                               << 16);
+        }
+    };
+
+    float yacc[TPW][4];
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) yacc[tp][v] = 0.0f;
+    // this lane's A operand within a slot: chunk 4 {0, 2, 1, 3}[g] + mu of
+    // group gl of its row (rows past MX read a row below MX; their outputs
+    // are dropped)
+    const int arow = nn & (MX - 1);
+    const int a_lane = (arow * kRowSlots + 4 * (((g & 1) << 1) | (g >> 1))) * 16;
+
+    auto process = [&](int b, int p, int slot) {
+        const int gl0 = g_begin + 2 * b;
+        const bool two = gl0 + 1 < g_end;
+        const unsigned char *sl = ring + slot * kChunk + a_lane;
+        bf16x8_t a0[4], a1[4];
+#pragma unroll
+        for (int mu = 0; mu < 4; ++mu) {
+            a0[mu] = *reinterpret_cast<const bf16x8_t *>(sl + mu * 16);
+            a1[mu] = *reinterpret_cast<const bf16x8_t *>(sl + (16 + mu) * 16);
+        }
+        unsigned wq[TPW][4];
+        float sc[TPW][2];
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            auto s02 = __builtin_amdgcn_permlane32_swap(cbuf[p][tp][0], cbuf[p][tp][2], false, false);
+            auto s13 = __builtin_amdgcn_permlane32_swap(cbuf[p][tp][1], cbuf[p][tp][3], false, false);
+            wq[tp][0] = s02[0];  // group 0, operand half 0 (the planes apply the slot flip)
+            wq[tp][1] = s13[0];
+            wq[tp][2] = s02[1];  // group 1
+            wq[tp][3] = s13[1];
+            const uint32_t pair = sbuf[p][tp];
+            sc[tp][0] = half_to_float((uint16_t)(pair & 0xffffu));
+            sc[tp][1] = two ? half_to_float((uint16_t)(pair >> 16)) : 0.0f;
+        }
+        load_block(b + kDist, (p + kDist) % PF);  // unconditional (clamped): exact load counts
+        f32x4_t acc0[TPW], acc1[TPW];
+        unsigned pl[TPW][4][4];
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            acc0[tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc1[tp] = acc0[tp];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) code_planes(wq[tp][w], kPlaneMask, pl[tp][w]);
+        }
+#pragma unroll
+        for (int mu = 0; mu < 4; ++mu)
+#pragma unroll
+            for (int tp = 0; tp < TPW; ++tp) {
+                acc0[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[mu], operand_from_planes(pl[tp][mu >> 1], mu & 1),
+                                                                   acc0[tp], 0, 0, 0);
+                acc1[tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a1[mu], operand_from_planes(pl[tp][2 + (mu >> 1)], mu & 1), acc1[tp], 0, 0, 0);
+            }
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                yacc[tp][v] = __builtin_fmaf(sc[tp][0], acc0[tp][v], yacc[tp][v]);
+                yacc[tp][v] = __builtin_fmaf(sc[tp][1], acc1[tp][v], yacc[tp][v]);
+            }
+    };
+
+    // One step: wait until this wave's loads of block s have landed (issued
+    // after them: two code refills and the loads of block s + 1), publish
+    // it with a barrier (which also says every wave is done reading the slot
+    // of block s - 1), refill that slot with block s + 2 (past the last block
+    // the last one again: the loads stay unconditional, so that the counts
+    // here and the compiler's own waits are exact), then compute block s.
+    auto step = [&](int s, int p, bool compute) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCodeOps + kLoads));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk(s + 2, (s + 2) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        if (compute) process(s, p, s % NS);
+    };
+
+    // prologue: blocks 0 and 1 of A, then of the codes
+    load_chunk(0, 0);
+    load_chunk(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < kDist; ++p) load_block(p, p);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // every K-group has at least bq blocks: those steps run unconditionally,
+    // unrolled by PF so that the code ring slot is a constant; the first br
+    // K-groups then have one more
+    const int nfull = (a.bq / PF) * PF;
+    for (int s0 = 0; s0 < nfull; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) step(s0 + p, p, true);
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (nfull + p < a.bq) step(nfull + p, p, true);
+    if (a.br > 0) {
+        const bool mine = kg < a.br;
+        switch (a.bq % PF) {
+        case 0: step(a.bq, 0, mine); break;
+        case 1: step(a.bq, 1, mine); break;
+        case 2: step(a.bq, 2, mine); break;
+        default: step(a.bq, 3, mine); break;
+        }
+    }
+    // every load to LDS has landed before the workgroup's LDS is reused
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+    // combine the K-groups' partial sums in a fixed order and store
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 4 * g + v;
+            if (i < MX) red[(((tw * wk + kg) * TPW + tp) * MX + i) * kTileN + nn] = yacc[tp][v];
+        }
+    __syncthreads();
+    const int outs = a.M * rows_per_wg;
+    for (int o = threadIdx.x; o < outs; o += blockDim.x) {
+        const int m = o / rows_per_wg, rem = o - m * rows_per_wg;
+        const int twi = rem / (kTileN * TPW), tp = (rem / kTileN) % TPW, j = rem % kTileN;
+        const int64_t n = n_wg + rem;
+        if (n >= a.N) continue;
+        float sum = 0.0f;
+        for (int w = 0; w < wk; ++w) sum += red[(((twi * wk + w) * TPW + tp) * MX + m) * kTileN + j];
+        const float out = -0.5f * sum;  // operands carried -2t
+        if (a.y_bf16)
+            static_cast<uint16_t *>(a.y)[(int64_t)m * a.N + n] = float_to_bf16_rne(out);
+        else
+            static_cast<float *>(a.y)[(int64_t)m * a.N + n] = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Signed normalized Walsh-Hadamard transform
 // ---------------------------------------------------------------------------
 //
@@ -1078,14 +1337,66 @@ int launch_gemv_mx(const GemvArgs &a, const GemvPlan &pl, hipStream_t stream)
     }
 }
 
+// bfloat16 activations with 5..16 rows: the A ring (gemv_ring_kernel), two
+// tiles per wave, codes two blocks ahead.  From a sweep of tile-waves (1, 2,
+// 4) x K-groups (1..4) x code blocks in flight (2..4) on the decode shapes:
+// one tile-wave, except two at 16 rows where that still leaves a workgroup
+// per CU (5120 -> 17408: 21.5 -> 19.7 us); two K-groups, four for long rows
+// (17408 -> 5120 at 16 rows: 24.4 -> 20.1 us); more code blocks in flight
+// were slower.
+struct RingPlan {
+    int wt, wk;
+    int64_t wgs;
+    size_t lds;
+};
+constexpr int kRingTpw = 2;
+
+inline bool plan_gemv_ring(int64_t N, int64_t K, int M, int mx, RingPlan &pl)
+{
+    const int64_t tiles = (N + kTileN - 1) / kTileN;
+    const int nblk = (int)((K / kGroup + 1) / 2);
+    if (K == 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+    pl.wt = (mx == 16 && (tiles + 2 * kRingTpw - 1) / (2 * kRingTpw) >= device_cus()) ? 2 : 1;
+    pl.wgs = (tiles + kRingTpw * pl.wt - 1) / (kRingTpw * pl.wt);
+    pl.wk = nblk >= 32 ? 4 : 2;
+    while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
+    const int loads = ((mx * 33 + 63) / 64 + pl.wt - 1) / pl.wt;  // as in gemv_ring_kernel
+    pl.lds = (size_t)pl.wk * 3 * loads * pl.wt * 1024 + (size_t)pl.wt * pl.wk * kRingTpw * mx * kTileN * sizeof(float);
+    return pl.lds <= kMaxLds;
+}
+
+template <int MX, int WT, int KD>
+int launch_gemv_ring(GemvArgs a, const RingPlan &pl, hipStream_t stream)
+{
+    const bool sc4 = (a.K / kGroup) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.scales) % 4) == 0;
+    void (*kernel)(GemvArgs) =
+        sc4 ? gemv_ring_kernel<MX, kRingTpw, WT, true, KD> : gemv_ring_kernel<MX, kRingTpw, WT, false, KD>;
+    int rc = ensure_lds(kernel, pl.lds);
+    if (rc) return rc;
+    a.wk = pl.wk;
+    a.wt = WT;
+    a.bq = a.nblk / pl.wk;
+    a.br = a.nblk % pl.wk;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * WT * pl.wk), pl.lds, stream, a);
+    return (int)hipGetLastError();
+}
+
 template <bool XF32>
 int launch_gemv_x(GemvArgs a, hipStream_t stream)
 {
     const int Mx = XF32 ? 2 * a.M : a.M;
     const int mx = Mx <= 1 ? 1 : Mx <= 2 ? 2 : Mx <= 4 ? 4 : Mx <= 8 ? 8 : 16;
+    if constexpr (!XF32) {
+        RingPlan rp;
+        if (mx >= 8 && plan_gemv_ring(a.N, a.K, a.M, mx, rp)) {
+            if (mx == 8) return launch_gemv_ring<8, 1, 2>(a, rp, stream);
+            return rp.wt == 2 ? launch_gemv_ring<16, 2, 2>(a, rp, stream) : launch_gemv_ring<16, 1, 2>(a, rp, stream);
+        }
+    }
     GemvPlan pl = plan_gemv(a.N, a.K, mx);
-    // direct A loads: bfloat16 with eight or more A rows, or any input whose
-    // staged image would not fit in LDS
+    // direct A loads: bfloat16 with eight or more A rows that the ring does
+    // not take (M K at or above 2^30 elements), or any input whose staged
+    // image would not fit in LDS
     if ((!XF32 && mx >= 8) || pl.lds > kMaxLds) pl = plan_gemv_ag(a.N, a.K, mx, XF32);
     switch (mx) {
     case 1: return launch_gemv_mx<1, XF32>(a, pl, stream);

@@ -189,6 +189,26 @@ def test_gemv_k_zero_gives_zeros(tern):
     assert (y.cpu() == 0).all()
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (5, 384, 16400),     # odd G: a one-group last block; one K-group; ragged last tile
+    (8, 1280, 16384),    # five blocks over two K-groups (one has an extra step)
+    (12, 2304, 16416),   # nine blocks: the unrolled loop's tail steps
+    (16, 5120, 16400),   # the sweep's row count, 16 rows
+    (9, 8448, 16384),    # 33 blocks: a full quad loop plus an extra step
+])
+def test_gemv_shared_activation_ring(tern, oracle_lib, M, K, N):
+    """bfloat16 activations with 5..16 rows on wide matrices take the kernel
+    whose tile-waves share an LDS ring of activation blocks; every output
+    element against the oracle."""
+    seed = 13 * M + K + N
+    print(f"gemv ring M={M} K={K} N={N} seed={seed}", flush=True)
+    codes_d, scales_d, t, s = full_problem(tern, seed, N, K, 1 / 3)
+    x = synth.activations_bf16(seed, M, K)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y, y_ref, bound, what=f"gemv ring M{M} K{K} N{N}")
+
+
 # Full sizes of the decode workloads, in the launch configuration the
 # benchmark uses: every output element against the (threaded) oracle.
 FULL = [(1, 1024, 1024, "f32", 1 / 3), (1, 4096, 12288, "f32", 0.35)] + \
