@@ -29,9 +29,9 @@
 // of four registers (one byte permute each), so the eight bfloat16 elements
 // of one MFMA B operand are weights i = 64c + 16g + 8h + 0..7 in order, and
 // the matching A operand is eight consecutive activations: a 16-byte chunk of
-// x, read from an LDS copy of x (up to four rows) or straight from memory
-// (more rows, where the copy would not fit or would be made by every
-// workgroup at a cost above the direct reads).
+// x.  Up to four rows, every workgroup copies x into LDS once.  From five
+// rows on (or where that copy would not fit), the tile-waves of a K-group
+// share an LDS ring of half superblocks of x instead (gemv_t5_ring_kernel).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -60,6 +60,7 @@ struct T5Args {
     int64_t N;
     int K, M, G, SB;
     int y_bf16;
+    int wk;                 // ring kernel: K-groups of a workgroup
 };
 
 // Operand patterns of the five digits of both 16-bit halves of each u[r];
@@ -91,7 +92,7 @@ __device__ __forceinline__ int t5_seg(int sb, int c, int j, int h, int g, int m,
     return ((((sb * 2 + c) * kT5Groups + j) * 2 + h) * 4 + g) * mx + m;
 }
 
-template <int MX, bool AG>
+template <int MX>
 __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
     const int sb_begin = (int)((int64_t)wave * a.SB / waves);
     const int sb_end = (int)((int64_t)(wave + 1) * a.SB / waves);
     u32x4_t *lds_x = reinterpret_cast<u32x4_t *>(smem);
-    float *red = reinterpret_cast<float *>(smem + (AG ? 0 : (size_t)a.SB * 80 * MX * 16));
+    float *red = reinterpret_cast<float *>(smem + (size_t)a.SB * 80 * MX * 16);
 
     // Code stream of this lane's row, one superblock ahead, by raw buffer
     // loads over the tile's rows (rows past N read zeros; their results are
@@ -134,31 +135,10 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
     };
     if (any) load_sb(sb_begin, cur0, cur1, csc);
 
-    // A operands.  Staged: unit = 8 consecutive k of one row (16 bytes),
-    // copied into the LDS image; the groups a short last superblock lacks
-    // are staged as zeros, so that their (unused) products are exact zeros.
-    // Direct: each lane reads its own chunks (rows past M read row M - 1,
-    // whose results are dropped; a group past G re-reads group G - 1, whose
-    // products meet a zero scale), one superblock ahead like the codes.
-    u32x4_t xa[2][2][kT5Groups], xn[2][2][kT5Groups];
-    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)a.x, (short)0, (int)((int64_t)a.M * a.K * 2), (int)kBufRaw);
-    const int xvo = ((a_active ? nn : a.M - 1) * a.K + 16 * g) * 2;
-    auto load_a = [&](int sb, u32x4_t (&dst)[2][2][kT5Groups]) {
-#pragma unroll
-        for (int j = 0; j < kT5Groups; ++j) {
-            const int gi = kT5Groups * sb + j < a.G ? kT5Groups * sb + j : a.G - 1;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    dst[c][h][j] = __builtin_bit_cast(
-                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo, 2 * (kGroup * gi + 64 * c + 8 * h), 0));
-        }
-    };
-    if constexpr (AG) {
-        if (any) load_a(sb_begin, xa);
-    } else {
+    // A operands: unit = 8 consecutive k of one row (16 bytes), copied into
+    // the LDS image; the groups a short last superblock lacks are staged as
+    // zeros, so that their (unused) products are exact zeros.
+    {
         const int upr = a.SB * 80;  // units per row, padded to whole superblocks
         const int units = a.M * upr;
         for (int u = threadIdx.x; u < units; u += blockDim.x) {
@@ -184,7 +164,6 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
         u32x4_t nxt0, nxt1;
         uint16_t nsc[kT5Groups];
         load_sb(sb + 1 < sb_end ? sb + 1 : sb, nxt0, nxt1, nsc);
-        if constexpr (AG) load_a(sb + 1 < sb_end ? sb + 1 : sb, xn);
         f32x4_t acc[kT5Groups];
 #pragma unroll
         for (int j = 0; j < kT5Groups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -195,12 +174,7 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
             for (int h = 0; h < 2; ++h) {
                 u32x4_t xs[kT5Groups];
 #pragma unroll
-                for (int j = 0; j < kT5Groups; ++j) {
-                    if constexpr (AG)
-                        xs[j] = xa[c][h][j];
-                    else
-                        xs[j] = a_active ? lds_x[t5_seg(sb, c, j, h, g, nn, MX)] : zero4;
-                }
+                for (int j = 0; j < kT5Groups; ++j) xs[j] = a_active ? lds_x[t5_seg(sb, c, j, h, g, nn, MX)] : zero4;
                 unsigned f[4][kT5Groups];
                 const unsigned d0 = cw[2 * h], d1 = cw[2 * h + 1];
                 // consecutive byte pairs into the 16-bit halves: bytes 0, 1 | 2, 3 | 4, 5 | 6, 7
@@ -225,14 +199,7 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
         }
         cur0 = nxt0;
         cur1 = nxt1;
-        if constexpr (AG) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int j = 0; j < kT5Groups; ++j) xa[c][h][j] = xn[c][h][j];
-        }
+
 #pragma unroll
         for (int j = 0; j < kT5Groups; ++j) csc[j] = nsc[j];
     }
@@ -258,10 +225,219 @@ __global__ __launch_bounds__(256) void gemv_t5_kernel(const T5Args a)
     }
 }
 
-size_t t5_lds(int64_t K, int mx, int waves, bool ag)
+// ---------------------------------------------------------------------------
+// Five or more rows: the A operands through a shared LDS ring
+// ---------------------------------------------------------------------------
+//
+// A workgroup is WT tile-waves x WK K-groups; the waves of a K-group own one
+// tile each over the same superblocks and take their A operands from an LDS
+// ring of three half superblocks of x (half c of superblock sb: the 64
+// activations k = 128 (5 sb + j) + 64 c + 0..63 of each of its five groups
+// j), filled by buffer loads to LDS two halves ahead.  A half holds its MX
+// rows in x's order, 40 16-byte chunks (chunk 8 j + q = k 128 (5 sb + j) +
+// 64 c + 8 q .. + 7) and one of padding per row, so a load instruction reads
+// contiguous 128-byte row spans and the 16 rows of an MFMA operand (chunk
+// 8 j + 2 g + h of its row) fall on 16 distinct bank groups.  Codes and
+// scales stream per wave one superblock ahead.  One barrier per half
+// publishes it and frees the slot read the half before.
+typedef __attribute__((address_space(3))) void lds_void_t;
+// s_waitcnt operand: vmcnt(n); expcnt and lgkmcnt not waited for
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kT5RowSlots = 41;  // 16-byte chunks per row of a half superblock: 40 and one of padding
+
+// One 16-byte buffer load per lane straight into LDS (lane l writes dst +
+// 16 l).  A plain device function: with the builtin written inside a kernel
+// template, the host pass of this compiler drops the template's launch stub.
+__device__ __forceinline__ void t5_load_lds16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+constexpr int t5_ring_loads(int mx, int wt) { return ((mx * kT5RowSlots + 63) / 64 + wt - 1) / wt; }
+
+template <int MX, int WT>
+__global__ __launch_bounds__(512) void gemv_t5_ring_kernel(const T5Args a)
+{
+    constexpr int NS = 3;                                // ring slots (half superblocks)
+    constexpr int kLoads = t5_ring_loads(MX, WT);        // loads to LDS per lane per half
+    constexpr int kChunk = kLoads * WT * 1024;           // LDS bytes of one half
+    constexpr int kCodeOps = 2 + kT5Groups;              // loads of one superblock's codes and scales
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wk = a.wk;
+    const int kg = wave / WT, tw = wave - kg * WT;
+    const int nn = lane & 15, g = lane >> 4;
+    const int sbq = a.SB / wk, sbr = a.SB % wk;  // every K-group has sbq (>= 1) or sbq + 1
+    const int sb_begin = kg * sbq + (kg < sbr ? kg : sbr);
+    const int nsb = sbq + (kg < sbr ? 1 : 0);
+    const int64_t n_wg = (int64_t)blockIdx.x * (kTileN * WT);
+    const int64_t n0 = n_wg + (int64_t)tw * kTileN;
+    unsigned char *ring = smem + (size_t)kg * NS * kChunk;
+    float *red = reinterpret_cast<float *>(smem + (size_t)wk * NS * kChunk);
+
+    // A chunks of this lane: slot p = (tw kLoads + q) 64 + lane of a half is
+    // chunk p % 41 of row p / 41.  Rows past M re-read row M - 1, padding
+    // slots and slots past the last row re-read chunk 0, and groups past G
+    // re-read group G - 1 (their scale is zero).
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.x, (short)0, (int)((int64_t)a.M * a.K * 2), (int)kBufRaw);
+    int xoff[kLoads], xj[kLoads];
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int p = (tw * kLoads + q) * 64 + lane;
+        const int row = p / kT5RowSlots, cs = p - row * kT5RowSlots;
+        const int r = row < a.M ? row : a.M - 1;
+        xj[q] = cs < 40 ? cs >> 3 : 0;
+        xoff[q] = r * a.K + (cs < 40 ? 8 * (cs & 7) : 0);
+    }
+    auto load_half = [&](int t, int slot) {
+        const int ls = t >> 1, c = t & 1;
+        const int sb = sb_begin + (ls < nsb ? ls : nsb - 1);
+        const int jmax = a.G - 1 - kT5Groups * sb;  // last group of the superblock (4 unless it is short)
+        unsigned char *dst = ring + slot * kChunk + tw * kLoads * 1024;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) {
+            const int j = xj[q] < jmax ? xj[q] : jmax;
+            t5_load_lds16(xrs, dst + 1024 * q, (xoff[q] + kGroup * j) * 2, (640 * sb + 64 * c) * 2);
+        }
+    };
+
+    // codes and scales of this wave's tile (rows past N read zeros; their
+    // results are dropped), one superblock ahead
+    const int64_t left = a.N - n0;
+    const int rows_here = left <= 0 ? 0 : (left < kTileN ? (int)left : kTileN);
+    const int rowb = a.SB * kT5Bytes;
+    const int64_t nb = rows_here > 0 ? n0 : 0;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.data + nb * rowb), (short)0, rows_here * rowb, (int)kBufRaw);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scales + nb * a.G), (short)0, rows_here * a.G * 2, (int)kBufRaw);
+    const int cvo = nn * rowb + 16 * g, svo = nn * a.G * 2;
+    u32x4_t cur0, cur1, nxt0, nxt1;
+    uint16_t csc[kT5Groups], nsc[kT5Groups];
+    auto load_sb = [&](int ls, u32x4_t &c0, u32x4_t &c1, uint16_t (&sh)[kT5Groups]) {
+        const int sb = sb_begin + (ls < nsb ? ls : nsb - 1);
+        c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, sb * kT5Bytes, 0));
+        c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, sb * kT5Bytes + 64, 0));
+#pragma unroll
+        for (int j = 0; j < kT5Groups; ++j) {
+            const int gi = kT5Groups * sb + j;
+            sh[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, 2 * (gi < a.G ? gi : a.G - 1), 0);
+        }
+    };
+
+    float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[kT5Groups];
+    const int arow = nn & (MX - 1);  // rows past MX read a row below MX; their outputs are dropped
+    const int a_lane = (arow * kT5RowSlots + 2 * g) * 16;
+
+    // half c of local superblock ls from ring slot `slot`
+    auto half = [&](int ls, int c, int slot) {
+        if (c == 0) {
+#pragma unroll
+            for (int j = 0; j < kT5Groups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const unsigned char *sl = ring + slot * kChunk + a_lane;
+        const u32x4_t cw = c ? cur1 : cur0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4_t xs[kT5Groups];
+#pragma unroll
+            for (int j = 0; j < kT5Groups; ++j) xs[j] = *reinterpret_cast<const u32x4_t *>(sl + (8 * j + h) * 16);
+            unsigned f[4][kT5Groups];
+            const unsigned d0 = cw[2 * h], d1 = cw[2 * h + 1];
+            const unsigned pairs[4] = {__builtin_amdgcn_perm(0u, d0, 0x0c010c00u),
+                                       __builtin_amdgcn_perm(0u, d0, 0x0c030c02u),
+                                       __builtin_amdgcn_perm(0u, d1, 0x0c010c00u),
+                                       __builtin_amdgcn_perm(0u, d1, 0x0c030c02u)};
+            t5_patterns(pairs, f);
+#pragma unroll
+            for (int j = 0; j < kT5Groups; ++j) {
+                const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, u32x4_t{f[0][j], f[1][j], f[2][j], f[3][j]});
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs[j]), wb, acc[j], 0, 0,
+                                                                 0);
+            }
+        }
+        if (c == 1) {
+            const int sb = sb_begin + ls;
+            const int p = (a.G - kT5Groups * sb) < kT5Groups ? (a.G - kT5Groups * sb) : kT5Groups;
+#pragma unroll
+            for (int j = 0; j < kT5Groups; ++j) {
+                const float sj = j < p ? half_to_float(csc[j]) : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) yacc[v] = __builtin_fmaf(sj, acc[j][v], yacc[v]);
+            }
+        }
+    };
+
+    // One half step t: wait until this wave's loads of half t have landed
+    // (issued after them: the loads of half t + 1 and one superblock of
+    // codes), publish it with a barrier (which also says every wave is done
+    // reading the slot of half t - 1), refill that slot with half t + 2
+    // (past the end the last one again: the loads stay unconditional, so
+    // the counts are exact), prefetch the next superblock's codes at the
+    // first half, then compute half t.
+    auto step = [&](int t, bool compute) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads + kCodeOps));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_half(t + 2, (t + 2) % NS);
+        if ((t & 1) == 0) load_sb((t >> 1) + 1, nxt0, nxt1, nsc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (compute) half(t >> 1, t & 1, t % NS);
+        if (t & 1) {
+            cur0 = nxt0;
+            cur1 = nxt1;
+#pragma unroll
+            for (int j = 0; j < kT5Groups; ++j) csc[j] = nsc[j];
+        }
+    };
+
+    load_half(0, 0);
+    load_half(1, 1);
+    load_sb(0, cur0, cur1, csc);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int ls = 0; ls < sbq; ++ls) {
+        step(2 * ls, true);
+        step(2 * ls + 1, true);
+    }
+    if (sbr > 0) {  // the first sbr K-groups have one more superblock
+        step(2 * sbq, kg < sbr);
+        step(2 * sbq + 1, kg < sbr);
+    }
+    // every load to LDS has landed before the workgroup's LDS is reused
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+    // combine the K-groups' partial sums in a fixed order and store
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int i = 4 * g + v;
+        if (i < MX) red[((tw * wk + kg) * MX + i) * kTileN + nn] = yacc[v];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < a.M * kTileN * WT; o += blockDim.x) {
+        const int m = o / (kTileN * WT), rem = o - m * (kTileN * WT);
+        const int twi = rem / kTileN, j = rem % kTileN;
+        const int64_t n = n_wg + rem;
+        if (n >= a.N) continue;
+        float sum = 0.0f;
+        for (int w = 0; w < wk; ++w) sum += red[((twi * wk + w) * MX + m) * kTileN + j];
+        const float out = -0.5f * sum;  // operands carried -2t
+        if (a.y_bf16)
+            static_cast<uint16_t *>(a.y)[(int64_t)m * a.N + n] = float_to_bf16_rne(out);
+        else
+            static_cast<float *>(a.y)[(int64_t)m * a.N + n] = out;
+    }
+}
+
+size_t t5_lds(int64_t K, int mx, int waves)
 {
     const int64_t SB = (K / kGroup + kT5Groups - 1) / kT5Groups;
-    return (ag ? 0 : (size_t)SB * 80 * mx * 16) + (size_t)waves * mx * kTileN * sizeof(float);
+    return (size_t)SB * 80 * mx * 16 + (size_t)waves * mx * kTileN * sizeof(float);
 }
 
 int t5_waves(int64_t K)
@@ -270,21 +446,36 @@ int t5_waves(int64_t K)
     return SB >= 4 ? 4 : (SB >= 1 ? (int)SB : 1);
 }
 
-// Direct A loads from five rows on (every workgroup would otherwise copy
-// 5..16 rows of x into LDS), or wherever the LDS copy would not fit.
-bool t5_direct(int64_t K, int mx) { return mx > 4 || t5_lds(K, mx, t5_waves(K), false) > kMaxLds; }
-
 template <int MX>
-int launch_t5_mx(const T5Args &a, hipStream_t stream)
+int launch_t5_staged(const T5Args &a, hipStream_t stream)
 {
     const int waves = t5_waves(a.K);
-    const bool ag = t5_direct(a.K, MX);
-    const size_t lds = t5_lds(a.K, MX, waves, ag);
-    void (*kernel)(T5Args) = ag ? gemv_t5_kernel<MX, true> : gemv_t5_kernel<MX, false>;
-    int rc = ensure_lds(kernel, lds);
+    const size_t lds = t5_lds(a.K, MX, waves);
+    int rc = ensure_lds(gemv_t5_kernel<MX>, lds);
     if (rc) return rc;
     const unsigned wgs = (unsigned)((a.N + kTileN - 1) / kTileN);
-    hipLaunchKernelGGL(kernel, dim3(wgs), dim3(64 * waves), lds, stream, a);
+    hipLaunchKernelGGL(gemv_t5_kernel<MX>, dim3(wgs), dim3(64 * waves), lds, stream, a);
+    return (int)hipGetLastError();
+}
+
+// Ring launch: two tile-waves; two K-groups, four for long rows (at least
+// one superblock each).  From a sweep of tile-waves (1, 2, 4) x K-groups
+// (1, 2, 4) at 16 rows: 17408 -> 5120 went 33.4 -> 23.9 us with two
+// tile-waves and four K-groups.
+template <int MX>
+int launch_t5_ring(T5Args a, hipStream_t stream)
+{
+    const int64_t tiles = (a.N + kTileN - 1) / kTileN;
+    constexpr int wt = 2;
+    int wk = a.SB >= 16 ? 4 : 2;
+    while (wk > 1 && a.SB < wk) wk /= 2;
+    a.wk = wk;
+    const size_t lds = (size_t)wk * 3 * t5_ring_loads(MX, wt) * wt * 1024 + (size_t)wt * wk * MX * kTileN * sizeof(float);
+    void (*kernel)(T5Args) = gemv_t5_ring_kernel<MX, wt>;
+    int rc = ensure_lds(kernel, lds);
+    if (rc) return rc;
+    const unsigned wgs = (unsigned)((tiles + wt - 1) / wt);
+    hipLaunchKernelGGL(kernel, dim3(wgs), dim3(64 * wt * wk), lds, stream, a);
     return (int)hipGetLastError();
 }
 
@@ -310,13 +501,23 @@ int launch_gemv_t5(const void *x, int M, int64_t K, const uint8_t *data, const u
     a.G = (int)(K / kGroup);
     a.SB = (int)((a.G + kT5Groups - 1) / kT5Groups);
     a.y_bf16 = y_bf16 ? 1 : 0;
+    a.wk = 1;
     const int mx = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    // up to four rows: each workgroup copies x into LDS, where that fits;
+    // otherwise the shared ring (rows padded to at least four)
+    if (mx <= 4 && t5_lds(K, mx, t5_waves(K)) <= kMaxLds) {
+        switch (mx) {
+        case 1: return launch_t5_staged<1>(a, st);
+        case 2: return launch_t5_staged<2>(a, st);
+        default: return launch_t5_staged<4>(a, st);
+        }
+    }
     switch (mx) {
-    case 1: return launch_t5_mx<1>(a, st);
-    case 2: return launch_t5_mx<2>(a, st);
-    case 4: return launch_t5_mx<4>(a, st);
-    case 8: return launch_t5_mx<8>(a, st);
-    default: return launch_t5_mx<16>(a, st);
+    case 1:
+    case 2:
+    case 4: return launch_t5_ring<4>(a, st);
+    case 8: return launch_t5_ring<8>(a, st);
+    default: return launch_t5_ring<16>(a, st);
     }
 }
 

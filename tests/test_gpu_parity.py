@@ -719,6 +719,27 @@ def test_gemv_t5_matches_oracle(tern, oracle_lib, M, K, N):
     assert_matmul_close(y, y_ref, bound, what=f"gemv_t5 M{M} K{K} N{N}")
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (5, 2048, 16400),    # last superblock holds one group; two tile-waves; ragged last tile
+    (16, 5120, 16400),   # two tile-waves, two K-groups
+    (12, 4096, 16400),   # seven superblocks over two K-groups (one has an extra one)
+    (16, 17408, 700),    # one tile-wave, four K-groups
+    (3, 20480, 300),     # few rows whose LDS copy of x would not fit: the ring
+])
+def test_gemv_t5_shared_activation_ring(tern, oracle_lib, M, K, N):
+    """Base-3 GEMV with 5..16 rows (or rows too long to copy into LDS) takes
+    the kernel whose tile-waves share an LDS ring of half superblocks of x;
+    every output element against the oracle."""
+    seed = 19 * M + K + N
+    print(f"gemv t5 ring M={M} K={K} N={N} seed={seed}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K)
+    y = _run_t5(tern, x, oracle_lib.t5_encode(t), s)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y, y_ref, bound, what=f"t5 ring M{M} K{K} N{N}")
+
+
 def test_gemv_t5_integer_exact_and_bf16_out(tern, oracle_lib):
     """Integer activations and scales in {0.5, 1, 2}: every partial sum is
     exact in binary32, so the result is bit-exact; bf16 output rounds once."""
