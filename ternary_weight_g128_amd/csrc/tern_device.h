@@ -106,6 +106,13 @@ int ensure_lds(Kernel kernel, size_t bytes)
     return 0;
 }
 
+// A workgroup wider than the kernel's __launch_bounds__ does not fit the
+// registers and barrier the kernel was built for: refused on the host.
+inline int check_block(unsigned threads, unsigned bound)
+{
+    return threads == 0 || threads > bound ? (int)hipErrorInvalidConfiguration : 0;
+}
+
 inline int device_cus()
 {
     static std::atomic<int> cus[64];

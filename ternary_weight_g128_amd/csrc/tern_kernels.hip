@@ -1323,6 +1323,7 @@ int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
     a.wt = pl.wt;
     a.bq = a.nblk / pl.wk;
     a.br = a.nblk % pl.wk;
+    if ((rc = check_block(64 * pl.wk * pl.wt, 512))) return rc;
     hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * pl.wk * pl.wt), pl.lds, stream, a);
     return (int)hipGetLastError();
 }
@@ -1343,7 +1344,9 @@ int launch_gemv_mx(const GemvArgs &a, const GemvPlan &pl, hipStream_t stream)
 // one tile-wave, except two at 16 rows where that still leaves a workgroup
 // per CU (5120 -> 17408: 21.5 -> 19.7 us); two K-groups, four for long rows
 // (17408 -> 5120 at 16 rows: 24.4 -> 20.1 us); more code blocks in flight
-// were slower.
+// were slower.  Short rows (under 32 blocks) with two or more workgroups per
+// CU run one wave per workgroup over all of K instead.  Workgroups stay
+// within the kernel's 512 threads (64 wt wk).
 struct RingPlan {
     int wt, wk;
     int64_t wgs;
@@ -1356,10 +1359,19 @@ inline bool plan_gemv_ring(int64_t N, int64_t K, int M, int mx, RingPlan &pl)
     const int64_t tiles = (N + kTileN - 1) / kTileN;
     const int nblk = (int)((K / kGroup + 1) / 2);
     if (K == 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
-    pl.wt = (mx == 16 && (tiles + 2 * kRingTpw - 1) / (2 * kRingTpw) >= device_cus()) ? 2 : 1;
+    const int64_t wgs1 = (tiles + kRingTpw - 1) / kRingTpw;  // workgroups of one tile-wave
+    if (nblk < 32 && wgs1 >= 2 * device_cus()) {
+        // short rows and two or more workgroups per CU: one wave each, the
+        // whole K range (5120 -> 17408: 16.2 -> 15.3 us at M = 8, 19.7 -> 18.8
+        // at M = 16)
+        pl.wt = 1;
+        pl.wk = 1;
+    } else {
+        pl.wt = (mx == 16 && (tiles + 2 * kRingTpw - 1) / (2 * kRingTpw) >= device_cus()) ? 2 : 1;
+        pl.wk = nblk >= 32 ? 4 : 2;
+        while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
+    }
     pl.wgs = (tiles + kRingTpw * pl.wt - 1) / (kRingTpw * pl.wt);
-    pl.wk = nblk >= 32 ? 4 : 2;
-    while (pl.wk > 1 && nblk < 2 * pl.wk) pl.wk /= 2;
     const int loads = ((mx * 33 + 63) / 64 + pl.wt - 1) / pl.wt;  // as in gemv_ring_kernel
     pl.lds = (size_t)pl.wk * 3 * loads * pl.wt * 1024 + (size_t)pl.wt * pl.wk * kRingTpw * mx * kTileN * sizeof(float);
     return pl.lds <= kMaxLds;
@@ -1377,6 +1389,7 @@ int launch_gemv_ring(GemvArgs a, const RingPlan &pl, hipStream_t stream)
     a.wt = WT;
     a.bq = a.nblk / pl.wk;
     a.br = a.nblk % pl.wk;
+    if ((rc = check_block(64 * WT * pl.wk, 512))) return rc;
     hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * WT * pl.wk), pl.lds, stream, a);
     return (int)hipGetLastError();
 }
@@ -1452,6 +1465,7 @@ int launch_rotate_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
     a.wt = pl.wt;
     a.bq = a.nblk / pl.wk;
     a.br = a.nblk % pl.wk;
+    if ((rc = check_block(64 * pl.wk, 512))) return rc;
     hipLaunchKernelGGL(kernel, dim3((unsigned)pl.wgs), dim3(64 * pl.wk), pl.lds, stream, a);
     return (int)hipGetLastError();
 }

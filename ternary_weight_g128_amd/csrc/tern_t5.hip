@@ -453,6 +453,7 @@ int launch_t5_staged(const T5Args &a, hipStream_t stream)
     const size_t lds = t5_lds(a.K, MX, waves);
     int rc = ensure_lds(gemv_t5_kernel<MX>, lds);
     if (rc) return rc;
+    if ((rc = check_block(64 * waves, 256))) return rc;
     const unsigned wgs = (unsigned)((a.N + kTileN - 1) / kTileN);
     hipLaunchKernelGGL(gemv_t5_kernel<MX>, dim3(wgs), dim3(64 * waves), lds, stream, a);
     return (int)hipGetLastError();
@@ -474,6 +475,7 @@ int launch_t5_ring(T5Args a, hipStream_t stream)
     void (*kernel)(T5Args) = gemv_t5_ring_kernel<MX, wt>;
     int rc = ensure_lds(kernel, lds);
     if (rc) return rc;
+    if ((rc = check_block(64 * wt * wk, 512))) return rc;
     const unsigned wgs = (unsigned)((tiles + wt - 1) / wt);
     hipLaunchKernelGGL(kernel, dim3(wgs), dim3(64 * wt * wk), lds, stream, a);
     return (int)hipGetLastError();
