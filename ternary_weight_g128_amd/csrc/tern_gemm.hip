@@ -11,21 +11,27 @@
 // each CU, so every SIMD runs one wave of each; their barriers are
 // independent, and one workgroup's barrier waits and VALU phases overlap the
 // other's matrix work.  One 128-K scale group is one pipeline stage: the
-// group's 64 x 128 activations (16 KiB) and the tile's 256 x 8 code words
-// (8 KiB) go straight from memory into LDS with buffer loads to LDS (no
-// register staging), three stages deep, two groups ahead of the matrix
-// cores.  Rows past M read as zero through the buffer's range check.
+// group's 64 x 128 activations (16 KiB) go straight from memory into LDS
+// with buffer loads to LDS (no register staging), three stages deep, two
+// groups ahead of the matrix cores.  The tile's code words travel two
+// groups at a time (256 columns x 16 words, 16 KiB, into one of two slots),
+// so each column's load is 64 contiguous bytes instead of 32: half the
+// requests per code byte on the CU's texture path.  Rows past M read as
+// zero through the buffer's range check.
 //
 // Operands.  For sub-tile column j, lane l holds output column l & 31 and
-// lane group g = l >> 5 loads code words 4g..4g+3 of that column's group.
-// Each word is first unshuffled (slots 0, 2, .., 14 to the low half, 1, 3,
-// .., 15 to the high half), so that the packed 16-bit shift of neg2t_pair
-// yields consecutive slot pairs: MFMA step kappa (0..7) then takes word
-// 4g + (kappa >> 1), half kappa & 1, and its B element e is weight
+// lane group g = l >> 5 reads code words 4g..4g+3 of that column's group.
+// Each word becomes four masked byte planes (code_planes: the flip, each
+// slot moved to bits 7..6 of a byte, and the zero-scale mask, together), and
+// each bfloat16 pair of the B operand is one byte permute of two planes
+// (operand_from_planes).  MFMA step kappa (0..7) takes word 4g + (kappa >> 1),
+// half kappa & 1, whose element e is slot 8 (kappa & 1) + e: weight
 // k = 64 g + 8 kappa + e of the group -- the same 8 consecutive k as the
 // 16-byte activation chunk c = 8 g + kappa.  In LDS, row r of a stage is
 // 256 bytes with chunk c stored at position c ^ (r & 15), which keeps the 16
-// lanes of an LDS read phase on distinct banks.
+// lanes of an LDS read phase on distinct banks; a column's 64 code bytes
+// hold 16-byte chunk q at position q ^ ((column >> 2) & 3), for the same
+// reason.
 //
 // Scales (Horner form).  An accumulator holds its output in units of the
 // current nonzero group scale s_c of its column: at a group boundary
@@ -50,6 +56,7 @@
 #include <cstdint>
 #include <mutex>
 #include <set>
+#include <type_traits>
 #include <utility>
 
 #include "tern_internal.h"
@@ -65,12 +72,14 @@ constexpr int kGemmWgPerCu = 2;                            // independent workgr
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
 constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
-constexpr int kGemmXBytes = kGemmBM * kGemmRowBytes;       // 16 KiB of activations
-constexpr int kGemmCBytes = kGemmBN * kWordsPerGroup * 4;  // 8 KiB of code words
-constexpr int kGemmStageBytes = kGemmXBytes + kGemmCBytes;
-constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);   // 4 (activations)
-constexpr int kGemmCDmaPerWave = kGemmCBytes / (kGemmThreads * 16);  // 2 (codes)
-static_assert(kGemmStages * kGemmStageBytes * kGemmWgPerCu <= 160 * 1024, "LDS for two workgroups per CU");
+constexpr int kGemmXBytes = kGemmBM * kGemmRowBytes;           // 16 KiB: one group of activations
+constexpr int kGemmCPairBytes = kGemmBN * 2 * kWordsPerGroup * 4;  // 16 KiB: code words of two groups
+constexpr int kGemmCSlots = 2;                                 // code pairs in LDS
+constexpr int kGemmCBase = kGemmStages * kGemmXBytes;          // code slots follow the activation stages
+constexpr int kGemmLdsBytes = kGemmCBase + kGemmCSlots * kGemmCPairBytes;  // 80 KiB
+constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);        // 4 (activations, every group)
+constexpr int kGemmCDmaPerWave = kGemmCPairBytes / (kGemmThreads * 16);   // 4 (codes, every other group)
+static_assert(kGemmLdsBytes * kGemmWgPerCu <= 160 * 1024, "LDS for two workgroups per CU");
 constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
 constexpr int kGemmMinPiece = 4;                           // groups per K piece, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
@@ -133,16 +142,17 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         const unsigned r = 4 * (kGemmDmaPerWave * wave + b) + (lane >> 4);
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
-    // Code words to LDS: wave instruction b fills 1 KiB = columns
-    // 64 wave + 32 b .. + 31 of the tile (32 bytes each: the group's 8
-    // words); lane l writes position l & 1 of column (l >> 1), which holds
-    // half (l & 1) ^ ((column >> 3) & 1) of the column's words, so that 16
-    // lanes reading the same half of 16 columns hit distinct banks.
+    // Code words of two groups to LDS: wave instruction b fills 1 KiB =
+    // columns 16 (4 wave + b) .. + 15 of the tile (64 bytes each: the two
+    // groups' 16 words, as four 16-byte chunks q = 2 (group in pair) +
+    // half); lane l writes position l & 3 of column (l >> 2), which holds
+    // chunk (l & 3) ^ ((column >> 2) & 3), so that 16 lanes reading the
+    // same chunk of 16 columns hit distinct banks.
     unsigned coff[kGemmCDmaPerWave];
 #pragma unroll
     for (int b = 0; b < kGemmCDmaPerWave; ++b) {
-        const unsigned c = 64 * wave + 32 * b + (lane >> 1);
-        coff[b] = c * (unsigned)(a.K / 4) + 16u * ((lane & 1) ^ ((c >> 3) & 1));
+        const unsigned c = 16 * (4 * wave + b) + (lane >> 2);
+        coff[b] = c * (unsigned)(a.K / 4) + 16u * ((lane & 3) ^ ((c >> 2) & 3));
     }
     // A operand reads: row 32 i + col, chunk 8 lg + kappa at position
     // (8 lg + kappa) ^ (col & 15)
@@ -175,26 +185,36 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         const uint32_t *ctile = a.codes + n0 * KW;
         const unsigned ctile_bytes = (unsigned)cols * (unsigned)(a.K / 4);
 
-        // group g of the tile's activations and code words into stage sb
-        // (columns past N read as zero words; their outputs are dropped)
-        auto stage = [&](int g, int sb) {
+        // group g of the tile's activations into stage sb, and the code
+        // words of groups g0, g0 + 1 into code slot cs (columns past N read
+        // as zero words, their outputs are dropped; a group past the piece
+        // reads words that are never used)
+        auto stage_x = [&](int g, int sb) {
             __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(xtile + (int64_t)g * kGroup), (short)0, (int)(tile_bytes - 256u * (unsigned)g),
                 (int)kBufferDword3);
-            unsigned char *dst = smem + sb * kGemmStageBytes + wave * (kGemmDmaPerWave * 1024);
+            unsigned char *dst = smem + sb * kGemmXBytes + wave * (kGemmDmaPerWave * 1024);
 #pragma unroll
             for (int b = 0; b < kGemmDmaPerWave; ++b)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 1024 * b), 16, voff[b], 0, 0, 0);
+        };
+        auto stage_c = [&](int g0, int cs) {
             __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(ctile + (int64_t)g * kWordsPerGroup), (short)0, (int)(ctile_bytes - 32u * (unsigned)g),
+                (void *)(ctile + (int64_t)g0 * kWordsPerGroup), (short)0, (int)(ctile_bytes - 32u * (unsigned)g0),
                 (int)kBufferDword3);
-            unsigned char *cdst = smem + sb * kGemmStageBytes + kGemmXBytes + wave * (kGemmCDmaPerWave * 1024);
+            unsigned char *cdst = smem + kGemmCBase + cs * kGemmCPairBytes + wave * (kGemmCDmaPerWave * 1024);
 #pragma unroll
             for (int b = 0; b < kGemmCDmaPerWave; ++b)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t *)(cdst + 1024 * b), 16, coff[b], 0, 0, 0);
         };
-        // this lane's four code words of sub-tile column j in stage sb
-        const unsigned c_lds = kGemmXBytes + (64 * wave + col) * 32 + 16 * (lg ^ ((col >> 3) & 1));
+        // this lane's four code words of sub-tile column j, first group of a
+        // pair, within a code slot (the second group: chunk position ^ 2)
+        unsigned c_lds[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const unsigned c = 64 * wave + 32 * j + col;
+            c_lds[j] = kGemmCBase + c * 64 + 16 * (lg ^ ((c >> 2) & 3));
+        }
 
         f32x16_t T[kGemmMI][2];
 #pragma unroll
@@ -208,10 +228,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         uint32_t s1[2];           // scale bits of group gg + 1
         auto gcl = [&](int g) { return g < kb ? g : kb - 1; };
 
-        // prologue: activations and codes of groups ka and ka + 1 (clamped)
-        // into stages 0 and 1; scales of groups ka and ka + 1
-        stage(ka, 0);
-        stage(gcl(ka + 1), 1);
+        // prologue: activations of groups ka and ka + 1 (clamped) into
+        // stages 0 and 1, their code words into slot 0; scales of groups ka
+        // and ka + 1
+        stage_x(ka, 0);
+        stage_x(gcl(ka + 1), 1);
+        stage_c(ka, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float s0 = half_to_float(srow[j][ka]);
@@ -222,17 +244,22 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        int sb = 0;
-        for (int gg = ka; gg < kb; ++gg) {
-            const unsigned char *cur = smem + sb * kGemmStageBytes;
+        int sb = 0;  // activation stage of group gg
+        int cs = 0;  // code slot of the pair holding group gg
+        // One group.  The first group of a pair (counted from ka) also
+        // issues the code words of the next pair, into the other slot.
+        auto group = [&](auto first_of_pair, int gg) {
+            constexpr bool kFirst = decltype(first_of_pair)::value;
+            const unsigned char *cur = smem + sb * kGemmXBytes;
+            const unsigned char *ccur = smem + cs * kGemmCPairBytes;
             const bool more = gg + 1 < kb;
             const int g2 = gcl(gg + 2);
             const int sb2 = sb == 0 ? 2 : sb - 1;            // (sb + 2) % 3
 
             // scales of group gg + 2 go out first (tiny loads); the stage
-            // of gg + 2 (activations and codes) is issued mid-group below,
-            // so that the waves' loads do not all queue at the CU's address
-            // unit at once
+            // of gg + 2 (activations, and the next pair's codes) is issued
+            // mid-group below, so that the waves' loads do not all queue at
+            // the CU's address unit at once
             uint32_t s2[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) s2[j] = srow[j][g2];
@@ -253,7 +280,8 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
 
             u32x4_t cw[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) cw[j] = *reinterpret_cast<const u32x4_t *>(cur + c_lds + 32 * 32 * j);
+            for (int j = 0; j < 2; ++j)
+                cw[j] = *reinterpret_cast<const u32x4_t *>(ccur + (c_lds[j] ^ (kFirst ? 0u : 32u)));
             const unsigned char *ap = cur + a_row;
             // activation operands one step ahead of the MFMAs that use them
             bf16x8_t aop[kGemmMI], anx[kGemmMI];
@@ -264,7 +292,8 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
             for (int q = 0; q < 4; ++q) {
                 if (q == 2) {
                     __builtin_amdgcn_sched_barrier(0);
-                    stage(g2, sb2);
+                    stage_x(g2, sb2);
+                    if constexpr (kFirst) stage_c(g2, cs ^ 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 unsigned t[2][4];
@@ -302,17 +331,25 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
                 mask[j] = mask_next[j];
             }
             // Everything but this group's stage loads has landed, in
-            // particular the stage of group gg + 1; a plain barrier (no
-            // memory fence, which would wait for those loads too) publishes
-            // it to all waves.  Every LDS read of this group was consumed
-            // above, so the stage refilled next group is free.
+            // particular the activations of group gg + 1 and, after the
+            // first group of a pair, the codes of the next pair; a plain
+            // barrier (no memory fence, which would wait for those loads
+            // too) publishes them to all waves.  Every LDS read of this
+            // group was consumed above, so the stages refilled next are free.
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave + kGemmCDmaPerWave));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave + (kFirst ? kGemmCDmaPerWave : 0)));
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             sb = sb == 2 ? 0 : sb + 1;
+            if constexpr (!kFirst) cs ^= 1;
+        };
+        int gg = ka;
+        for (; gg + 1 < kb; gg += 2) {
+            group(std::true_type{}, gg);
+            group(std::false_type{}, gg + 1);
         }
+        if (gg < kb) group(std::true_type{}, gg);
 
         // epilogue: lane (col, lg) of sub-tile (i, j) holds rows
         // 32 i + 8 (v >> 2) + 4 lg + (v & 3), column 64 wave + 32 j + col
@@ -501,7 +538,7 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
     a.scales = scales;
     a.y = y;
     a.partial = static_cast<float *>(workspace);
-    const size_t lds = kGemmStages * (size_t)kGemmStageBytes;
+    const size_t lds = kGemmLdsBytes;
     int rc = ensure_lds(gemm_kernel, lds);
     if (rc) return rc;
     hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
