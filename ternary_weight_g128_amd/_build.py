@@ -18,6 +18,7 @@ SOURCES = [
     ("tern_kernels.hip", []),
     ("tern_gemm.hip", ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]),
     ("tern_t5.hip", []),
+    ("tern_gemv1.hip", []),
     ("tern_api.cpp", []),
     ("tern_codec.cpp", []),
 ]

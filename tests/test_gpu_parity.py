@@ -209,6 +209,36 @@ def test_gemv_shared_activation_ring(tern, oracle_lib, M, K, N):
     assert_matmul_close(y, y_ref, bound, what=f"gemv ring M{M} K{K} N{N}")
 
 
+EVEN_SPLIT = [
+    # (M, K, N)
+    (1, 896, 3),       # four blocks (the fewest this kernel takes), one quad, one workgroup
+    (1, 896, 1027),    # a ragged last quad
+    (1, 3968, 7777),   # 31 groups: a one-group last block, unpaired scale loads, ragged quads
+    (1, 2048, 1030),   # fewer quads than CUs
+    (1, 5120, 5123),   # the 5120-row projection plus a ragged quad
+    (1, 12288, 999),   # long rows, few quads: many steps per quad
+    (2, 896, 1027), (3, 3968, 777), (4, 2048, 4099), (2, 8192, 1999), (4, 12288, 517), (3, 1024, 5),
+]
+
+
+@pytest.mark.parametrize("M,K,N", EVEN_SPLIT)
+def test_gemv_even_split(tern, oracle_lib, M, K, N):
+    """One to four rows of bfloat16 x, with a multiple of four 256-K blocks
+    per row, take the kernel that splits (quad, block) pairs evenly over the
+    CUs, four blocks per MFMA; every element against the oracle, fp32 and
+    bf16 outputs, and a repeat is bit-identical."""
+    seed = 31 * K + N + M
+    print(f"gemv even split M={M} K={K} N={N} seed={seed}", flush=True)
+    codes_d, scales_d, t, s = full_problem(tern, seed, N, K, 1 / 3)
+    x = synth.activations_bf16(seed, M, K)
+    y = _run_gemv(tern, x, codes_d, scales_d)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y, y_ref, bound, what=f"even split M{M} K{K} N{N}")
+    assert np.array_equal(y, _run_gemv(tern, x, codes_d, scales_d)), "repeat differs"
+    yb = _run_gemv(tern, x, codes_d, scales_d, ydt="bf16")
+    assert_matmul_close(yb, y_ref, bound, bf16_out=True, what=f"even split bf16 M{M} K{K} N{N}")
+
+
 # Full sizes of the decode workloads, in the launch configuration the
 # benchmark uses: every output element against the (threaded) oracle.
 FULL = [(1, 1024, 1024, "f32", 1 / 3), (1, 4096, 12288, "f32", 0.35)] + \
