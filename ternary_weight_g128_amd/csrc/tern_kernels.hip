@@ -1308,6 +1308,20 @@ inline GemvPlan plan_gemv_ag(int64_t N, int64_t K, int mx, bool x_f32)
     return pl;
 }
 
+// Whether the tiled kernel's workgroups (bfloat16 x, M <= 4) would leave the
+// busiest CU more than 5% above the average: then the even-split kernel
+// (tern_gemv1.hip) runs instead.  Measured at M = 1: 17408 -> 5120, 320
+// tiles, 11.7 -> 9.7 us; 5120 -> 34816, 1088 workgroups, 15.8 -> 14.0 us;
+// 4096 -> 12288, 768 workgroups (three per CU), tiled 7.0 us against 7.3.
+inline bool gemv_tiles_uneven(int64_t N, int64_t K, int M)
+{
+    const int mx = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    const GemvPlan pl = plan_gemv(N, K, mx);
+    const int64_t cus = device_cus();
+    const int64_t rounds = (pl.wgs + cus - 1) / cus;
+    return (double)rounds * (double)cus > 1.05 * (double)pl.wgs;
+}
+
 template <int MX, bool XF32, int TPW>
 int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
@@ -1524,7 +1538,7 @@ int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *cod
                 const uint16_t *scales, int64_t N, void *y, bool y_bf16, void *stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!x_f32 && tern::gemv1_applies(M, N, K))
+    if (!x_f32 && M <= 4 && gemv_tiles_uneven(N, K, M) && tern::gemv1_applies(M, N, K))
         return tern::launch_gemv1(x, M, K, codes, scales, N, y, y_bf16, stream);
     const int step = gemv_rows_per_launch(N, K, x_f32);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
