@@ -41,8 +41,8 @@ def parse():
     p.add_argument("--reps", type=int, default=7,
                    help="timed replays of the headline graph (each after a cache flush)")
     p.add_argument("--workload", default="rotated",
-                   choices=["rotated", "sweep", "prefill", "chain", "base3", "tiny", "floor", "copy"],
-                   help="rotated: the headline step; sweep / prefill / chain / base3 / tiny: extra "
+                   choices=["rotated", "sweep", "prefill", "chain", "base3", "binary", "tiny", "floor", "copy"],
+                   help="rotated: the headline step; sweep / prefill / chain / base3 / binary / tiny: extra "
                         "measurements; floor: load-only kernels over the decode byte counts; "
                         "copy: a plain device copy of known size (counter calibration)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -550,6 +550,55 @@ def bench_t5(tern, torch, synth, steps):
     return out
 
 
+def b1_gemv_bytes(M, K, N):
+    """Algorithmic bytes of a GEMV over the binary variant: K/8 bytes of sign
+    bits per row, FP16 scales, bf16 activations, fp32 output."""
+    return N * K // 8 + 2 * N * K // 128 + M * K * 2 + M * N * 4
+
+
+def bench_b1(tern, torch, synth, steps):
+    """Decode GEMV over the binary variant (1.125 bits/weight) beside the
+    2-bit GEMV on the same +-1 weights (their ternary codes), M = 1 and 4,
+    rotated pools, graph-timed."""
+    out = {}
+    for (K, N) in ((5120, 17408), (17408, 5120)):
+        seed = 11 + K
+        b = synth.ternary(seed, N, K, 0.0)
+        s = synth.scales_f16(seed, N, K)
+        bits = tern.tern_pack_b1(b)
+        b0 = torch.from_numpy(bits.view(np.int32)).cuda()
+        s0 = torch.from_numpy(s.view(np.int16)).cuda()
+        copies = max(2, -(-POOL_BYTES // (bits.nbytes + s.nbytes)))
+        pool = [(b0, s0)] + [(b0.clone(), s0.clone()) for _ in range(copies - 1)]
+        pool2 = make_pool(tern, torch, b, s, tern.tern_codes_bytes(N, K) + tern.tern_scales_bytes(N, K))
+        for M in (1, 4):
+            x = synth.activations_bf16(seed, M, K)
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+            def fn(i, xd=xd, y=y):
+                w, s_ = pool[i % len(pool)]
+                tern.tern_gemv_b1(xd, w, s_, out=y)
+
+            def fn2(i, xd=xd, y=y):
+                c, s_ = pool2[i % len(pool2)]
+                tern.tern_gemv(xd, c, s_, out=y)
+
+            for i in range(5):
+                fn(i)
+                fn2(i)
+            ms, _, _ = time_graph(torch, fn, steps)
+            ms2, _, _ = time_graph(torch, fn2, steps)
+            us, us2 = 1e3 * ms / steps, 1e3 * ms2 / steps
+            gbs = b1_gemv_bytes(M, K, N) / (us * 1e-6) / 1e9
+            out[f"M{M}_K{K}_N{N}"] = {"us": us, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                      "bytes": b1_gemv_bytes(M, K, N), "us_2bit": us2,
+                                      "bytes_2bit": gemv_bytes(M, K, N, 2)}
+        del pool, pool2, b0, s0
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill(tern, torch, synth, steps):
     out = {}
     for w in synth.PREFILL:
@@ -668,6 +717,9 @@ def main():
     if args.workload == "base3":
         print(json.dumps({"base3": bench_t5(tern, torch, synth, args.steps)}))
         return
+    if args.workload == "binary":
+        print(json.dumps({"binary": bench_b1(tern, torch, synth, args.steps)}))
+        return
 
     w, host, res = bench_rotated(args, tern, torch, synth)
     line = {
@@ -698,6 +750,7 @@ def main():
             "prefill_gemm": bench_prefill(tern, torch, synth, 20),
             "decode_pass_27b_class": bench_chain(tern, torch, synth),
             "decode_gemv_base3": bench_t5(tern, torch, synth, 200),
+            "decode_gemv_binary": bench_b1(tern, torch, synth, 200),
         }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, host)

@@ -273,6 +273,23 @@ tern_status tern_gemv(const void *x, int xdt, int64_t M, int64_t K,
 tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uint8_t *data,
                          const uint16_t *scales, int64_t N, void *y, int ydt, void *stream);
 
+/* Decode-regime matmul over the binary variant ("prism-ml/Ternary-Bonsai-
+ * 27B-mlx-2bit" model card, "Benchmarks", the 1-bit row: one sign bit per
+ * weight plus the binary16 scale of each 128 weights, 1.125 bits/weight):
+ * y[m][n] = sum_g s[n][g] sum_{k in g} b[n][k] x[m][k], with b = +1 for a
+ * set bit and -1 for a clear one, in the word layout of tern_pack_b1.  The
+ * words are streamed as they are (no 2-bit expansion) and turned into
+ * operands in the kernel; the same accuracy as tern_gemv.
+ * x: [M][K] TERN_BF16, 16-byte aligned, M <= 4; bits [N][K/32] 16-byte
+ * aligned; scales [N][K/128] 2-byte aligned; K a multiple of 1024; y [M][N]
+ * written as ydt (TERN_F32, or TERN_BF16 rounded to nearest even).
+ * Errors: TERN_EINVAL (sizes, alignment, NULL), TERN_EUNSUPPORTED (M > 4,
+ * TERN_F32 activations, K not a multiple of 1024, an output dtype other
+ * than TERN_F32 / TERN_BF16, or K too long for the kernel's LDS image of x:
+ * about 38000 at M = 4), TERN_EDEVICE. */
+tern_status tern_gemv_b1(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *bits,
+                         const uint16_t *scales, int64_t N, void *y, int ydt, void *stream);
+
 /* Rotated decode in one launch: y = (H_b D x / sqrt(b)) (s_g t)^T, i.e. the
  * signed normalized Walsh-Hadamard transform of tern_fwht (forward, blocks
  * of b along K) followed by the tern_gemv matmul on the rotated binary32

@@ -33,6 +33,7 @@ EXPORTED = [
     "tern_mlx_export", "tern_mlx_import", "tern_b1_bytes", "tern_pack_b1", "tern_unpack_b1",
     "tern_b1_to_codes", "tern_codes_to_b1", "tern_mlx_export_b1", "tern_mlx_import_b1",
     "tern_t5_bytes", "tern_pack_t5", "tern_unpack_t5", "tern_gemv_t5", "tern_gemm_noalloc",
+    "tern_gemv_b1",
 ]
 _SIZE_FNS = ("tern_codes_bytes", "tern_scales_bytes", "tern_gemm_workspace_bytes",
              "tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes")
@@ -67,6 +68,7 @@ _lib.tern_gemm_workspace_bytes.restype = _SZ
 _lib.tern_gemm.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]
 _lib.tern_gemm_noalloc.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _P]
 _lib.tern_gemv_t5.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
+_lib.tern_gemv_b1.argtypes = [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I, _P]
 for _name in ("tern_scales_g64_bytes", "tern_b1_bytes", "tern_t5_bytes"):
     getattr(_lib, _name).argtypes = [_I64, _I64]
     getattr(_lib, _name).restype = _SZ
@@ -450,6 +452,25 @@ def tern_gemv_t5(x, data, scales, out=None, out_dtype=None, stream=None):
     _shape_check("tern_gemv_t5", "out", out, (M, N), (2, 4), x.device)
     _check(_lib.tern_gemv_t5(_dev_ptr(x), _dt(x), M, K, _dev_ptr(data), _dev_ptr(scales), N,
                              _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv_t5")
+    return out
+
+
+def tern_gemv_b1(x, bits, scales, out=None, out_dtype=None, stream=None):
+    """y [M, N] = x [M, K] (bfloat16, M <= 4, K a multiple of 1024) times the
+    binary variant's weights (bits int32 [N, K/32] on the device, as
+    tern_pack_b1 writes them) with their group scales."""
+    T = _torch()
+    M, K = _dims2("tern_gemv_b1", x)
+    N = bits.shape[0]
+    if K % TERN_GROUP:
+        raise ValueError(f"tern_gemv_b1: K = {K} is not a multiple of {TERN_GROUP}")
+    if out is None:
+        out = T.empty((M, N), dtype=out_dtype or T.float32, device=x.device)
+    _shape_check("tern_gemv_b1", "bits", bits, (N, K // 32), (4,), x.device)
+    _shape_check("tern_gemv_b1", "scales", scales, (N, K // TERN_GROUP), (2,), x.device)
+    _shape_check("tern_gemv_b1", "out", out, (M, N), (2, 4), x.device)
+    _check(_lib.tern_gemv_b1(_dev_ptr(x), _dt(x), M, K, _dev_ptr(bits), _dev_ptr(scales), N,
+                             _dev_ptr(out), _dt(out), _stream_ptr(stream)), "tern_gemv_b1")
     return out
 
 

@@ -204,6 +204,58 @@ tern_status tern_gemm_noalloc(const void *x, int xdt, int64_t M, int64_t K, cons
     return device_status(tern::launch_gemm_noalloc(x, M, K, codes, scales, N, y, stream), "tern_gemm_noalloc");
 }
 
+tern_status tern_gemv_b1(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *bits,
+                         const uint16_t *scales, int64_t N, void *y, int ydt, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) {
+        set_error("tern_gemv_b1: negative size");
+        return TERN_EINVAL;
+    }
+    if (K % TERN_GROUP != 0) {
+        set_error("tern_gemv_b1: K must be a multiple of 128 (whole scale groups)");
+        return TERN_EINVAL;
+    }
+    if (M > 4) {
+        set_error("tern_gemv_b1: M must be at most 4");
+        return TERN_EUNSUPPORTED;
+    }
+    if (xdt != TERN_BF16) {
+        set_error("tern_gemv_b1: activations must be TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (ydt != TERN_F32 && ydt != TERN_BF16) {
+        set_error("tern_gemv_b1: output dtype must be TERN_F32 or TERN_BF16");
+        return TERN_EUNSUPPORTED;
+    }
+    if (K % 1024 != 0) {
+        set_error("tern_gemv_b1: K must be a multiple of 1024 (four 256-K blocks per step)");
+        return TERN_EUNSUPPORTED;
+    }
+    if (M == 0 || N == 0) return TERN_OK;
+    if (K == 0) {
+        set_error("tern_gemv_b1: K must be positive");
+        return TERN_EUNSUPPORTED;
+    }
+    if (!x || !bits || !scales || !y) {
+        set_error("tern_gemv_b1: NULL pointer");
+        return TERN_EINVAL;
+    }
+    if (!aligned(x, 16) || !aligned(bits, 16) || !aligned(scales, 2) || !aligned(y, ydt == TERN_F32 ? 4 : 2)) {
+        set_error("tern_gemv_b1: x and bits must be 16-byte aligned, scales 2-byte, y to its dtype");
+        return TERN_EINVAL;
+    }
+    if (N > ((int64_t)1 << 31) - 64 || K > TERN_MAX_K) {
+        set_error("tern_gemv_b1: matrix too large");
+        return TERN_EINVAL;
+    }
+    if (!tern::gemv1_applies((int)M, N, K)) {
+        set_error("tern_gemv_b1: shape not supported (activation image beyond LDS, or offsets beyond 32 bits)");
+        return TERN_EUNSUPPORTED;
+    }
+    return device_status(tern::launch_gemv1(x, (int)M, K, bits, scales, N, y, ydt == TERN_BF16, true, stream),
+                         "tern_gemv_b1");
+}
+
 tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uint8_t *data,
                          const uint16_t *scales, int64_t N, void *y, int ydt, void *stream)
 {

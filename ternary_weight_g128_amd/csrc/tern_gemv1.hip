@@ -62,10 +62,11 @@ constexpr int kBlockX = 256;                    // activations per block
 constexpr int kXBlockBytes = 2 * kBlockX + 16;  // LDS bytes per block of x (16 of padding)
 constexpr int kPF = 4;                          // code ring slots
 constexpr unsigned kBufRaw1 = 0x00020000u;      // raw buffer resource, 32-bit data format
+typedef unsigned u32x2v_t __attribute__((ext_vector_type(2)));
 
 struct Gemv1Args {
     const uint16_t *x;       // bfloat16 [M][K]
-    const uint32_t *codes;   // [N][K / 16]
+    const uint32_t *codes;   // [N][K / 16] 2-bit codes, or [N][K / 32] sign bits (binary)
     const uint16_t *scales;  // [N][K / 128]
     void *y;                 // [M][N] binary32 or bfloat16
     int64_t N;
@@ -79,9 +80,34 @@ struct Gemv1Args {
     int y_bf16;
 };
 
+// Binary weights (the 1-bit variant: bit j of word w of a row is weight
+// 32 w + j, 1 for +1 and 0 for -1).  Byte plane j of a word holds, in byte
+// b, 0x40 | (bit 8 b + j) << 7: the high byte of the bfloat16 -2t (0xC000
+// for +1, 0x4000 for -1), so that one byte permute of two planes gives a
+// bfloat16 pair of the MFMA operand, as for the 2-bit codes.
+__device__ __forceinline__ void bin_planes(unsigned w, unsigned (&p)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = ((w << (7 - j)) & 0x80808080u) | 0x40404040u;
+}
+
+// MFMA B operand of weights 8 mu + 0..7 of a binary word (element e = bit
+// 8 mu + e): pair i is byte mu of planes 2 i and 2 i + 1 in bytes 1 and 3.
+__device__ __forceinline__ bf16x8_t bin_operand(const unsigned (&p)[8], int mu)
+{
+    const unsigned sel = 0x0Cu | ((unsigned)mu << 8) | (0x0Cu << 16) | ((4u + (unsigned)mu) << 24);
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_perm(p[2 * i + 1], p[2 * i], sel);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // SC4: the scale pair of a block is one aligned 4-byte load (G even).
 // KD: steps of codes in flight.  MX: rows of x the sums are kept for (M <= MX).
-template <bool SC4, int KD, int MX>
+// BIN: binary weights (a block of a row is 8 words; lane group g loads words
+// 2 g, 2 g + 1 and one v_permlane32_swap leaves it word {0, 2, 1, 3}[g] of
+// each of the block's two groups), else 2-bit codes.
+template <bool SC4, int KD, int MX, bool BIN>
 __global__ __launch_bounds__(512) void gemv1_kernel(const Gemv1Args a)
 {
     static_assert(KD >= 1 && KD < kPF, "the refill reuses a consumed slot");
@@ -138,28 +164,36 @@ __global__ __launch_bounds__(512) void gemv1_kernel(const Gemv1Args a)
     //    (their outputs are dropped), and refills past the wave's last step
     //    are never used.  The loads stay unconditional, so the waits for
     //    them are exact.
-    const int wpr = a.K / 16;
+    constexpr int kWordsPerBlock = BIN ? 8 : 16;  // words of one row per 256-K block
+    const int wpr = BIN ? a.K / 32 : a.K / 16;
     const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t *>(a.codes), (short)0, (int)(a.N * wpr * 4), (int)kBufRaw1);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.scales), (short)0, (int)(a.N * a.G * 2), (int)kBufRaw1);
-    const int lane_w = 4 * (r * wpr + 16 * slice + 4 * g);  // bytes: row r, block slice, words 4 g..
+    // bytes: row r, block slice, words 4 g.. (binary: 2 g..)
+    const int lane_w = 4 * (r * wpr + kWordsPerBlock * slice + (BIN ? 2 : 4) * g);
     const int lane_s = 2 * (r * a.G + 2 * slice);
     int lq = j_lo / spq, lb = kSlices * (j_lo - lq * spq);   // next load: quad, first block
     u32x4_t cbuf[kPF];
     uint32_t sbuf[kPF];
     auto load_step = [&](int p) {
         const int row = ((int)q_begin + lq) * 4;
-        const int uw = 4 * (row * wpr + 16 * lb), us = 2 * (row * a.G + 2 * lb);
+        const int uw = 4 * (row * wpr + kWordsPerBlock * lb), us = 2 * (row * a.G + 2 * lb);
         int lw = lane_w;
         bool two = true;
-        if constexpr (!SC4) {
+        if constexpr (!SC4 && !BIN) {
             // odd G: the last block holds one group; its upper lanes re-read
-            // that group (its second scale is zeroed below)
+            // that group (its second scale is zeroed below); binary rows
+            // always hold whole blocks
             two = 2 * (lb + slice) + 1 < a.G;
             lw = two ? lane_w : lane_w - 16 * (g & 2);
         }
-        cbuf[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, uw + lw, 0, 0));
+        if constexpr (BIN) {
+            const u32x2v_t w2 = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(crs, uw + lw, 0, 0));
+            cbuf[p] = u32x4_t{w2[0], w2[1], 0u, 0u};
+        } else {
+            cbuf[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, uw + lw, 0, 0));
+        }
         if constexpr (SC4) {
             sbuf[p] = __builtin_amdgcn_raw_buffer_load_b32(srs, us + lane_s, 0, 0);
         } else {
@@ -220,23 +254,45 @@ __global__ __launch_bounds__(512) void gemv1_kernel(const Gemv1Args a)
                 a1[mu] = *reinterpret_cast<const bf16x8_t *>(src + second + 16 * mu);
             }
         }
-        const auto s02 = __builtin_amdgcn_permlane32_swap(cbuf[p][0], cbuf[p][2], false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(cbuf[p][1], cbuf[p][3], false, false);
-        const unsigned wq[4] = {s02[0], s13[0], s02[1], s13[1]};  // group 0 halves, group 1 halves
+        unsigned wq[4];
+        if constexpr (BIN) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(cbuf[p][0], cbuf[p][1], false, false);
+            wq[0] = sw[0];  // group 0 word
+            wq[1] = sw[1];  // group 1 word
+            wq[2] = wq[3] = 0u;
+        } else {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(cbuf[p][0], cbuf[p][2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(cbuf[p][1], cbuf[p][3], false, false);
+            wq[0] = s02[0];  // group 0 halves, group 1 halves
+            wq[1] = s13[0];
+            wq[2] = s02[1];
+            wq[3] = s13[1];
+        }
         const uint32_t sp = sbuf[p];
         const float sc0 = half_to_float((uint16_t)(sp & 0xffffu));
         const float sc1 = half_to_float((uint16_t)(sp >> 16));
         load_step((p + KD) % kPF);  // unconditional: exact load counts
-        unsigned pl[4][4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) code_planes(wq[w], kPlaneMask, pl[w]);
         f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        if constexpr (BIN) {
+            unsigned b0[8], b1[8];
+            bin_planes(wq[0], b0);
+            bin_planes(wq[1], b1);
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[mu], operand_from_planes(pl[mu >> 1], mu & 1), acc0,
-                                                           0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[mu], operand_from_planes(pl[2 + (mu >> 1)], mu & 1),
-                                                           acc1, 0, 0, 0);
+            for (int mu = 0; mu < 4; ++mu) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[mu], bin_operand(b0, mu), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[mu], bin_operand(b1, mu), acc1, 0, 0, 0);
+            }
+        } else {
+            unsigned pl[4][4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) code_planes(wq[w], kPlaneMask, pl[w]);
+#pragma unroll
+            for (int mu = 0; mu < 4; ++mu) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[mu], operand_from_planes(pl[mu >> 1], mu & 1),
+                                                               acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a1[mu], operand_from_planes(pl[2 + (mu >> 1)], mu & 1), acc1, 0, 0, 0);
+            }
         }
         if (pq != qcur) {  // the wave moved to the next quad (uniform)
             if (sum_lane) flush();
@@ -318,9 +374,10 @@ bool plan_gemv1(int M, int64_t N, int64_t K, Gemv1Plan &pl)
 }
 
 template <int MX>
-void (*gemv1_pick(bool sc4))(Gemv1Args)
+void (*gemv1_pick(bool sc4, bool bin))(Gemv1Args)
 {
-    return sc4 ? gemv1_kernel<true, 2, MX> : gemv1_kernel<false, 2, MX>;
+    if (bin) return sc4 ? gemv1_kernel<true, 2, MX, true> : gemv1_kernel<false, 2, MX, true>;
+    return sc4 ? gemv1_kernel<true, 2, MX, false> : gemv1_kernel<false, 2, MX, false>;
 }
 
 }  // namespace
@@ -334,10 +391,10 @@ bool gemv1_applies(int M, int64_t N, int64_t K)
 }
 
 int launch_gemv1(const void *x, int M, int64_t K, const uint32_t *codes, const uint16_t *scales, int64_t N,
-                 void *y, bool y_bf16, void *stream)
+                 void *y, bool y_bf16, bool binary, void *stream)
 {
     Gemv1Plan pl;
-    if (!plan_gemv1(M, N, K, pl)) return (int)hipErrorInvalidValue;
+    if (!plan_gemv1(M, N, K, pl) || (binary && (K / kGroup) % 2 != 0)) return (int)hipErrorInvalidValue;
     Gemv1Args a;
     a.x = static_cast<const uint16_t *>(x);
     a.codes = codes;
@@ -354,7 +411,7 @@ int launch_gemv1(const void *x, int M, int64_t K, const uint32_t *codes, const u
     a.y_bf16 = y_bf16 ? 1 : 0;
     const bool sc4 = a.G % 2 == 0 && (reinterpret_cast<uintptr_t>(scales) % 4) == 0;
     void (*kernel)(Gemv1Args) =
-        pl.mx == 1 ? gemv1_pick<1>(sc4) : pl.mx == 2 ? gemv1_pick<2>(sc4) : gemv1_pick<4>(sc4);
+        pl.mx == 1 ? gemv1_pick<1>(sc4, binary) : pl.mx == 2 ? gemv1_pick<2>(sc4, binary) : gemv1_pick<4>(sc4, binary);
     int rc = ensure_lds(kernel, pl.lds);
     if (rc) return rc;
     if ((rc = check_block(64 * pl.waves, 512))) return rc;

@@ -23,10 +23,11 @@ int launch_rotate_gemv(const void *x, bool x_f32, const int8_t *signs, int block
                        void *stream);
 size_t rotate_gemv_lds(int64_t M, int64_t N, int64_t K);
 // GEMV of one to four rows of bfloat16 x with the work split evenly over
-// the CUs (tern_gemv1.hip): whether it takes this shape, and the launch.
+// the CUs (tern_gemv1.hip): whether it takes this shape, and the launch;
+// `binary`: the weights are the 1-bit variant's sign words (K / 128 even).
 bool gemv1_applies(int M, int64_t N, int64_t K);
 int launch_gemv1(const void *x, int M, int64_t K, const uint32_t *codes, const uint16_t *scales, int64_t N,
-                 void *y, bool y_bf16, void *stream);
+                 void *y, bool y_bf16, bool binary, void *stream);
 size_t max_lds_bytes();
 int launch_fwht(const void *x, bool x_f32, const int8_t *signs, int64_t M, int64_t K,
                 int block, bool inverse, float *y, void *stream);

@@ -1539,7 +1539,7 @@ int launch_gemv(const void *x, bool x_f32, int M, int64_t K, const uint32_t *cod
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!x_f32 && M <= 4 && gemv_tiles_uneven(N, K, M) && tern::gemv1_applies(M, N, K))
-        return tern::launch_gemv1(x, M, K, codes, scales, N, y, y_bf16, stream);
+        return tern::launch_gemv1(x, M, K, codes, scales, N, y, y_bf16, false, stream);
     const int step = gemv_rows_per_launch(N, K, x_f32);
     const size_t xsz = x_f32 ? 4 : 2, ysz = y_bf16 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += step) {

@@ -98,6 +98,26 @@ def test_gemv_t5_empty_is_noop(tern):
     assert _gemv_t5(tern, N=0, x=NULL, data=NULL, scales=NULL, y=NULL) == 0
 
 
+def _gemv_b1(tern, x=A16, xdt=1, M=1, K=1024, bits=A16, scales=A16, N=16, y=A16, ydt=0):
+    return tern.lib().tern_gemv_b1(x, xdt, M, K, bits, scales, N, y, ydt, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=5), 4), (dict(M=-1), 1), (dict(N=-3), 1), (dict(K=100), 1), (dict(K=640), 4),
+    (dict(xdt=0), 4), (dict(ydt=2), 4), (dict(x=NULL), 1), (dict(bits=NULL), 1),
+    (dict(scales=NULL), 1), (dict(y=NULL), 1), (dict(x=A2), 1), (dict(bits=A2), 1),
+    (dict(K=1 << 31), 1), (dict(K=0), 4),
+])
+def test_gemv_b1_rejects(tern, kw, status):
+    assert _gemv_b1(tern, **kw) == status
+    assert tern.tern_last_error().startswith("tern_gemv_b1")
+
+
+def test_gemv_b1_empty_is_noop(tern):
+    assert _gemv_b1(tern, M=0, x=NULL, bits=NULL, scales=NULL, y=NULL) == 0
+    assert _gemv_b1(tern, N=0, x=NULL, bits=NULL, scales=NULL, y=NULL) == 0
+
+
 def _gemm(tern, x=A16, xdt=1, M=64, K=128, codes=A16, scales=A16, N=16, y=A16, ws=NULL, wsb=0):
     return tern.lib().tern_gemm(x, xdt, M, K, codes, scales, N, y, ws, wsb, NULL)
 

@@ -716,6 +716,66 @@ def test_format_variant_through_kernels(tern, oracle_lib, fmt, M, K, N, op):
 
 
 # ---------------------------------------------------------------------------
+# decode GEMV over the binary variant (one sign bit per weight)
+# ---------------------------------------------------------------------------
+
+B1_SHAPES = [
+    # (M, K, N): four blocks (the fewest), ragged quads, fewer quads than CUs,
+    # rows of 32 and more blocks, the decode shapes
+    (1, 1024, 5), (1, 1024, 1027), (2, 2048, 4099), (3, 4096, 777), (4, 8192, 517),
+    (1, 5120, 17408), (1, 17408, 5120), (4, 5120, 12288), (2, 17408, 333),
+]
+
+
+@pytest.mark.parametrize("M,K,N", B1_SHAPES)
+def test_gemv_b1_matches_oracle(tern, oracle_lib, M, K, N):
+    """tern_gemv_b1 streams the 1-bit words of tern_pack_b1 as they are; every
+    element against the oracle's product of the same +-1 weights (as ternary
+    values) and scales; bf16 output; a repeat is bit-identical."""
+    seed = 57 * M + K + 3 * N
+    print(f"gemv_b1 M={M} K={K} N={N} seed={seed}", flush=True)
+    T = torch()
+    b = synth.ternary(seed, N, K, 0.0)  # +-1 only
+    s = synth.scales_f16(seed, N, K)
+    bits = tern.tern_pack_b1(b)
+    bits_d = T.from_numpy(bits.view(np.int32)).cuda()
+    scales_d = T.from_numpy(s.view(np.int16)).cuda()
+    x = synth.activations_bf16(seed, M, K)
+    xd = x_to_device(x)
+    y = tern.tern_gemv_b1(xd, bits_d, scales_d)
+    T.cuda.synchronize()
+    y = y_to_host(y)
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(b), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y, y_ref, bound, what=f"gemv_b1 M{M} K{K} N{N}")
+    y2 = tern.tern_gemv_b1(xd, bits_d, scales_d)
+    T.cuda.synchronize()
+    assert np.array_equal(y, y_to_host(y2)), "repeat differs"
+    yb = tern.tern_gemv_b1(xd, bits_d, scales_d, out_dtype=T.bfloat16)
+    T.cuda.synchronize()
+    assert_matmul_close(y_to_host(yb), y_ref, bound, bf16_out=True, what=f"gemv_b1 bf16 M{M} K{K} N{N}")
+
+
+def test_gemv_b1_same_as_ternary_codes(tern):
+    """The binary words and their 2-bit expansion (tern_b1_to_codes) through
+    tern_gemv give bit-identical results for integer-valued inputs, where
+    every sum is exact."""
+    T = torch()
+    M, K, N, seed = 2, 3072, 700, 91
+    b = synth.ternary(seed, N, K, 0.0)
+    s = np.full((N, K // 128), 0x3C00, dtype=np.uint16)  # 1.0
+    x32 = np.random.default_rng(seed).integers(-8, 9, size=(M, K)).astype(np.float32)
+    x = (x32.view(np.uint32) >> 16).astype(np.uint16)    # exact in bfloat16
+    bits = tern.tern_pack_b1(b)
+    xd = x_to_device(x)
+    y1 = tern.tern_gemv_b1(xd, T.from_numpy(bits.view(np.int32)).cuda(), T.from_numpy(s.view(np.int16)).cuda())
+    codes_d, scales_d = tern.to_device(tern.tern_b1_to_codes(bits, K), s)
+    y2 = tern.tern_gemv(xd, codes_d, scales_d)
+    T.cuda.synchronize()
+    assert np.array_equal(y_to_host(y1), y_to_host(y2))
+    assert np.array_equal(y_to_host(y1), (x32.astype(np.float64) @ b.T.astype(np.float64)).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
 # decode GEMV over the base-3 layout (five ternary values per byte)
 # ---------------------------------------------------------------------------
 
