@@ -622,6 +622,47 @@ def test_rotated_step_graph_replays_match_eager(tern):
         T.cuda.synchronize()
 
 
+def test_even_split_graph_replays_match_eager(tern):
+    """Two chained even-split GEMV links (bf16 output feeding the next link)
+    and a binary GEMV captured in one HIP graph: every replay, with eager
+    work in between, equals the eager calls."""
+    T = torch()
+    seed, M = 43, 2
+    (K1, N1), (K2, N2) = (2048, 3072), (3072, 1000)   # uneven tile splits: the even-split kernel
+    c1, s1 = pack_to_device(tern, synth.ternary(seed, N1, K1), synth.scales_f16(seed, N1, K1))
+    c2, s2 = pack_to_device(tern, synth.ternary(seed + 1, N2, K2), synth.scales_f16(seed + 1, N2, K2))
+    bits = T.from_numpy(tern.tern_pack_b1(synth.ternary(seed + 2, N2, K2, 0.0)).view(np.int32)).cuda()
+    xd = x_to_device(synth.activations_bf16(seed, M, K1))
+    h = T.empty((M, N1), dtype=T.bfloat16, device="cuda")
+    y = T.empty((M, N2), dtype=T.float32, device="cuda")
+    yb = T.empty((M, N2), dtype=T.float32, device="cuda")
+
+    def step():
+        tern.tern_gemv(xd, c1, s1, out=h)
+        tern.tern_gemv(h, c2, s2, out=y)
+        tern.tern_gemv_b1(h, bits, s2, out=yb)
+
+    step()
+    T.cuda.synchronize()
+    y_eager, yb_eager = y.clone(), yb.clone()
+    g = T.cuda.CUDAGraph()
+    st = T.cuda.Stream()
+    st.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(st):
+        with T.cuda.graph(g, stream=st):
+            step()
+    T.cuda.current_stream().wait_stream(st)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        yb.fill_(float("nan"))
+        h.zero_()
+        other = T.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, y_eager) and T.equal(yb, yb_eager), f"replay {rep} differs"
+        assert T.isfinite(other)
+
+
 def test_gemm_graph_replays_match_eager(tern):
     """tern_gemm with split tiles (workspace + fixup pass) captured in a HIP
     graph: every replay, with eager work in between, equals the eager call."""
