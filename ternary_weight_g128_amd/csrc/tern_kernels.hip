@@ -1325,7 +1325,9 @@ inline bool gemv_tiles_uneven(int64_t N, int64_t K, int M)
 template <int MX, bool XF32, int TPW>
 int launch_gemv_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
-    const bool sc4 = (a.K / kGroup) % 2 == 0;
+    // scale pairs as one 4-byte load: G even and the scales 4-byte aligned
+    // (the ABI asks only for 2)
+    const bool sc4 = (a.K / kGroup) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.scales) % 4) == 0;
     void (*kernel)(GemvArgs) = sc4 ? gemv_kernel<MX, XF32, TPW, true> : gemv_kernel<MX, XF32, TPW, false>;
     // binary32 direct loads run one tile per wave (two would spill registers)
     if constexpr (!(XF32 && TPW > 1))
@@ -1470,7 +1472,7 @@ void (*rotate_kernel(int tpw, bool sc4))(GemvArgs)
 template <int MX, int ROT>
 int launch_rotate_t(GemvArgs a, const GemvPlan &pl, hipStream_t stream)
 {
-    const bool sc4 = (a.K / kGroup) % 2 == 0;
+    const bool sc4 = (a.K / kGroup) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.scales) % 4) == 0;
     void (*kernel)(GemvArgs) = a.log2b == 12 ? rotate_kernel<MX, ROT, 12>(pl.tpw, sc4)
                                              : rotate_kernel<MX, ROT, 0>(pl.tpw, sc4);
     int rc = ensure_lds(kernel, pl.lds);

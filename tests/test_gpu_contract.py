@@ -103,3 +103,65 @@ def test_gemv_f32_activations_beyond_lds(tern, oracle_lib, M):
     torch().cuda.synchronize()
     y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K)
     assert_matmul_close(y_to_host(y), y_ref, bound, what=f"gemv f32 K{K} M{M}")
+
+
+def _offset_scales(T, scales_d):
+    """The same scale values at a 2-byte (not 4-byte) aligned address: the
+    ABI asks scales to be 2-byte aligned only."""
+    N, G = scales_d.shape
+    buf = T.empty(N * G + 1, dtype=scales_d.dtype, device=scales_d.device)
+    view = buf[1:].view(N, G)
+    view.copy_(scales_d)
+    assert view.data_ptr() % 4 == 2
+    return view
+
+
+def test_scales_two_byte_aligned_every_entry_point(tern):
+    """Every matmul entry point gives bit-identical results when its scales
+    sit at an address that is 2-byte but not 4-byte aligned (the kernels
+    then build each scale pair from two 2-byte loads)."""
+    T = torch()
+    seed = 71
+    cases = [  # (what, M, K, N, x dtype): each kernel family
+        ("tiled, binary32 x", 1, 2048, 700, "f32"),
+        ("tiled, two rows, three blocks", 2, 768, 300, "bf16"),
+        ("even split", 1, 4096, 1000, "bf16"),
+        ("activation ring", 8, 2048, 4100, "bf16"),
+    ]
+    for what, M, K, N, xdt in cases:
+        print(f"scales offset: gemv {what} M={M} K={K} N={N}", flush=True)
+        t = synth.ternary(seed, N, K)
+        s = synth.scales_f16(seed, N, K)
+        codes_d, scales_d = pack_to_device(tern, t, s)
+        xd = x_to_device(_x(seed, M, K, xdt))
+        y0 = tern.tern_gemv(xd, codes_d, scales_d)
+        y1 = tern.tern_gemv(xd, codes_d, _offset_scales(T, scales_d))
+        T.cuda.synchronize()
+        assert T.equal(y0, y1), what
+    # fused rotation
+    K, N = 4096, 1000
+    t = synth.ternary(seed, N, K)
+    s = synth.scales_f16(seed, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    xd = x_to_device(synth.activations_bf16(seed, 1, K))
+    dd = T.from_numpy(synth.signs(seed, K)).cuda()
+    y0 = tern.tern_rotate_gemv(xd, dd, 4096, codes_d, scales_d)
+    y1 = tern.tern_rotate_gemv(xd, dd, 4096, codes_d, _offset_scales(T, scales_d))
+    T.cuda.synchronize()
+    assert T.equal(y0, y1), "rotate_gemv"
+    # binary variant
+    bits = T.from_numpy(tern.tern_pack_b1(synth.ternary(seed, N, K, 0.0)).view(np.int32)).cuda()
+    y0 = tern.tern_gemv_b1(xd, bits, scales_d)
+    y1 = tern.tern_gemv_b1(xd, bits, _offset_scales(T, scales_d))
+    T.cuda.synchronize()
+    assert T.equal(y0, y1), "gemv_b1"
+    # prefill GEMM
+    M, K, N = 100, 1024, 300
+    t = synth.ternary(seed, N, K)
+    s = synth.scales_f16(seed, N, K)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    xd = x_to_device(synth.activations_bf16(seed, M, K))
+    y0 = tern.tern_gemm(xd, codes_d, scales_d)
+    y1 = tern.tern_gemm(xd, codes_d, _offset_scales(T, scales_d))
+    T.cuda.synchronize()
+    assert T.equal(y0, y1), "gemm"
