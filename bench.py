@@ -184,26 +184,52 @@ def per_step_us(stats):
             "p90_us": 1e3 * stats["p90_ms"] / n, "replays": stats["replays"], "steps_per_replay": n}
 
 
+def _gpu_sysfs_dir(torch):
+    """The sysfs directory of device 0 (its PCI address from the device
+    properties), or the only DRM card with clock tables; None if neither."""
+    import glob
+    p = torch.cuda.get_device_properties(0)
+    bus = getattr(p, "pci_bus_id", None)
+    if bus is not None:
+        d = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0) or 0, bus,
+                                                      getattr(p, "pci_device_id", 0) or 0)
+        if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+            return d
+    cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return os.path.dirname(cards[0]) if len(cards) == 1 else None
+
+
+def _dpm_level(path):
+    """The current level of a pp_dpm_* table (the line marked '*')."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].replace("*", "").strip()
+    except OSError:
+        return None
+    return None
+
+
 def clocks_under_load(torch, g, replay_ms, seconds=1.5):
-    """GPU clocks read with rocm-smi while the timed graph replays back to
-    back (about `seconds` of queued GPU work), so the clocks are the ones the
-    kernels run at.  Returns the parsed sclk / mclk lines (or the error)."""
-    import subprocess
+    """GPU clocks read from the device's sysfs clock tables while the timed
+    graph replays back to back (about `seconds` of queued GPU work), so the
+    clocks are the ones the kernels run at (no helper process is started).
+    Returns the current sclk / mclk levels (or the reason they are missing)."""
     n = int(max(1, seconds * 1e3 / max(replay_ms, 1e-3)))
     n = min(n, 20000)
+    d = _gpu_sysfs_dir(torch)
     for _ in range(n):
         g.replay()
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
-    except (OSError, subprocess.SubprocessError) as e:
-        torch.cuda.synchronize()
-        return {"error": str(e)}
-    torch.cuda.synchronize()
     res = {}
-    for line in out.splitlines():
+    if d is not None:
         for key in ("sclk", "mclk", "fclk", "socclk"):
-            if key in line and "(" in line:
-                res[key] = line.split("(")[-1].rstrip(")").strip()
+            v = _dpm_level(os.path.join(d, "pp_dpm_" + key))
+            if v is not None:
+                res[key] = v
+    torch.cuda.synchronize()
+    if not res:
+        res["error"] = "no readable clock table for device 0"
     res["replays_queued"] = n
     return res
 
