@@ -152,8 +152,12 @@ def time_graph(torch, fn, steps, reps=3):
     times, timing each replay with HIP events on the replay stream.  One
     untimed replay uploads the graph first; before every timed replay the
     flusher streams 1 GiB through L2 and the MALL, so no timed replay finds
-    the weights it reads in a cache (whatever the step count).  Returns the
-    median replay time in ms, the graph, and median / p10 / p90."""
+    the weights it reads in a cache (whatever the step count).  The flush,
+    the start event, the replay and the end event are queued together
+    (the flush keeps the GPU busy while the host submits the replay), so the
+    interval between the events is the GPU time of the steps alone, not the
+    host's submission of the graph.  Returns the median replay time in ms,
+    the graph, and median / p10 / p90."""
     g = capture(torch, fn, steps)
     g.replay()                       # upload / first replay, untimed
     torch.cuda.synchronize()
@@ -161,10 +165,10 @@ def time_graph(torch, fn, steps, reps=3):
     cur = torch.cuda.current_stream()
     times = []
     for _ in range(reps):
-        fl()
-        torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        fl()
         start.record(cur)
         g.replay()
         end.record(cur)
