@@ -285,8 +285,9 @@ tern_status tern_gemv_t5(const void *x, int xdt, int64_t M, int64_t K, const uin
  * written as ydt (TERN_F32, or TERN_BF16 rounded to nearest even).
  * Errors: TERN_EINVAL (sizes, alignment, NULL), TERN_EUNSUPPORTED (M > 4,
  * TERN_F32 activations, K not a multiple of 1024, an output dtype other
- * than TERN_F32 / TERN_BF16, or K too long for the kernel's LDS image of x:
- * about 38000 at M = 4), TERN_EDEVICE. */
+ * than TERN_F32 / TERN_BF16, or a shape whose LDS image of x and per-
+ * workgroup sums exceed one workgroup's LDS: K beyond about 38000 at M = 4,
+ * or, for rows of 8192 or more, N beyond about 250000), TERN_EDEVICE. */
 tern_status tern_gemv_b1(const void *x, int xdt, int64_t M, int64_t K, const uint32_t *bits,
                          const uint16_t *scales, int64_t N, void *y, int ydt, void *stream);
 
