@@ -5,19 +5,21 @@
 // "CUDA (NVIDIA GPUs)": codes unpacked and scaled inside the kernel, never a
 // dense FP16 weight tensor).  bfloat16 activations, binary32 result.
 //
-// Tiles.  A workgroup of four waves computes a 64 (m) x 256 (n) output
-// tile; wave w owns columns 64w .. 64w + 63 as 2 x 2 sub-tiles of
-// v_mfma_f32_32x32x16_bf16 (accumulators in VGPRs).  Two workgroups share
-// each CU, so every SIMD runs one wave of each; their barriers are
-// independent, and one workgroup's barrier waits and VALU phases overlap the
-// other's matrix work.  One 128-K scale group is one pipeline stage: the
-// group's 64 x 128 activations (16 KiB) go straight from memory into LDS
-// with buffer loads to LDS (no register staging), three stages deep, two
-// groups ahead of the matrix cores.  The tile's code words travel two
-// groups at a time (256 columns x 16 words, 16 KiB, into one of two slots),
-// so each column's load is 64 contiguous bytes instead of 32: half the
-// requests per code byte on the CU's texture path.  Rows past M read as
-// zero through the buffer's range check.
+// Tiles.  A workgroup of four waves computes a 128 (m) x 128 (n) output
+// tile; wave w owns columns 32w .. 32w + 31 as four 32-row sub-tiles of
+// v_mfma_f32_32x32x16_bf16 (accumulators in VGPRs), so each weight operand
+// it unpacks feeds four MFMAs.  Two workgroups share each CU, so every SIMD
+// runs one wave of each; their barriers are independent, and one
+// workgroup's barrier waits and VALU phases overlap the other's matrix
+// work.  One 128-K scale group is one pipeline stage: the group's 128 x 128
+// activations (32 KiB) go straight from memory into LDS with buffer loads
+// to LDS (no register staging), two stages, one group ahead of the matrix
+// cores; the loads are spread over the first half of the group's MFMA steps.
+// The tile's code words travel two groups at a time (128 columns x 16
+// words, 8 KiB, into one of two slots), so each column's load is 64
+// contiguous bytes instead of 32: half the requests per code byte on the
+// CU's texture path.  Rows past M read as zero through the buffer's range
+// check.
 //
 // Operands.  For sub-tile column j, lane l holds output column l & 31 and
 // lane group g = l >> 5 reads code words 4g..4g+3 of that column's group.
@@ -65,22 +67,30 @@ namespace {
 
 #include "tern_device.h"
 
-constexpr int kGemmMI = 2;                                 // 32-row sub-tiles per wave
-constexpr int kGemmWaves = 4;                              // one per 64 output columns
-constexpr int kGemmBM = 32 * kGemmMI, kGemmBN = 64 * kGemmWaves;
+// Tile shape: MI 32-row and NJ 32-column sub-tiles per wave, four waves
+// side by side along N, two activation stages in LDS.
+template <int MI_, int NJ_>
+struct GemmCfg {
+    static constexpr int MI = MI_, NJ = NJ_;
+    static constexpr int kWaves = 4;
+    static constexpr int BM = 32 * MI, BN = 32 * NJ * kWaves;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kRowBytes = kGroup * 2;                        // one group of a bf16 row
+    static constexpr int kXBytes = BM * kRowBytes;                      // one group of activations
+    static constexpr int kCPairBytes = BN * 2 * kWordsPerGroup * 4;     // code words of two groups
+    static constexpr int kCBase = 2 * kXBytes;                          // code slots follow the stages
+    static constexpr int kLdsBytes = kCBase + 2 * kCPairBytes;          // two code slots
+    static constexpr int kDmaPerWave = kXBytes / (kThreads * 16);       // activation loads per group
+    static constexpr int kCDmaPerWave = kCPairBytes / (kThreads * 16);  // code loads per pair
+    static constexpr int kTileElems = BM * BN;
+    static_assert(kLdsBytes * 2 <= 160 * 1024, "LDS for two workgroups per CU");
+};
+// 128 x 128 tiles: each wave 128 x 32, so one weight operand feeds four
+// MFMAs
+typedef GemmCfg<4, 1> GemmTile;
 constexpr int kGemmWgPerCu = 2;                            // independent workgroups per CU
-constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kGemmStages = 3;                             // x prefetched two groups ahead
-constexpr int kGemmRowBytes = kGroup * 2;                  // one group of a bf16 row
-constexpr int kGemmXBytes = kGemmBM * kGemmRowBytes;           // 16 KiB: one group of activations
-constexpr int kGemmCPairBytes = kGemmBN * 2 * kWordsPerGroup * 4;  // 16 KiB: code words of two groups
-constexpr int kGemmCSlots = 2;                                 // code pairs in LDS
-constexpr int kGemmCBase = kGemmStages * kGemmXBytes;          // code slots follow the activation stages
-constexpr int kGemmLdsBytes = kGemmCBase + kGemmCSlots * kGemmCPairBytes;  // 80 KiB
-constexpr int kGemmDmaPerWave = kGemmXBytes / (kGemmThreads * 16);        // 4 (activations, every group)
-constexpr int kGemmCDmaPerWave = kGemmCPairBytes / (kGemmThreads * 16);   // 4 (codes, every other group)
-static_assert(kGemmLdsBytes * kGemmWgPerCu <= 160 * 1024, "LDS for two workgroups per CU");
-constexpr int kGemmTileElems = kGemmBM * kGemmBN;          // outputs per tile
+constexpr int kGemmThreads = GemmTile::kThreads;
+constexpr int kGemmTileElems = GemmTile::kTileElems;       // outputs per tile
 constexpr int kGemmMinPiece = 4;                           // groups per K piece, at least
 constexpr unsigned kBufferDword3 = 0x00020000u;            // raw buffer, 32-bit data format
 // s_waitcnt operand: vmcnt(n), expcnt and lgkmcnt not waited for
@@ -105,20 +115,34 @@ struct GemmArgs {
     int64_t items;          // r * s leftover pieces
 };
 
-// Position in the tile of accumulator element e in MFMA register order
-// e = ((((wave * MI + i) * 2 + j) * 16 + v) * 64 + lane): lane (c, g) of
-// sub-tile (i, j) holds row 32 i + 8 (v >> 2) + 4 g + (v & 3), column
-// 64 wave + 32 j + c.
-__device__ __forceinline__ void gemm_elem_pos(int e, int &mr, int &nc)
+// One 16-byte buffer load per lane straight into LDS (lane l writes dst +
+// 16 l).  A plain device function: with the builtin written inside a kernel
+// template, the host pass of this compiler drops the template's launch stub.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, unsigned voff)
 {
-    const int lane = e & 63, v = (e >> 6) & 15, j = (e >> 10) & 1;
-    const int i = (e >> 11) % kGemmMI, wave = (e >> 11) / kGemmMI;
-    mr = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    nc = 64 * wave + 32 * j + (lane & 31);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, 0, 0, 0);
 }
 
+// Position in the tile of accumulator element e in MFMA register order
+// e = ((((wave * MI + i) * NJ + j) * 16 + v) * 64 + lane): lane (c, g) of
+// sub-tile (i, j) holds row 32 i + 8 (v >> 2) + 4 g + (v & 3), column
+// 32 (NJ wave + j) + c.
+template <class C>
+__device__ __forceinline__ void gemm_elem_pos(int e, int &mr, int &nc)
+{
+    const int lane = e & 63, v = (e >> 6) & 15, ij = e >> 10;
+    const int j = ij % C::NJ, i = (ij / C::NJ) % C::MI, wave = ij / (C::NJ * C::MI);
+    mr = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    nc = 32 * (C::NJ * wave + j) + (lane & 31);
+}
+
+template <class C>
 __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const GemmArgs a)
 {
+    constexpr int MI = C::MI, NJ = C::NJ;
+    constexpr int kGemmBM = C::BM, kGemmBN = C::BN, kGemmRowBytes = C::kRowBytes, kGemmXBytes = C::kXBytes;
+    constexpr int kGemmCPairBytes = C::kCPairBytes, kGemmCBase = C::kCBase;
+    constexpr int kGemmDmaPerWave = C::kDmaPerWave, kGemmCDmaPerWave = C::kCDmaPerWave;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,6 +151,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
     const int64_t KW = a.K / 16;
     const unsigned row_bytes = 2u * (unsigned)a.K;
 
+    // The hardware deals workgroups to the eight XCDs round robin
+    // (blockIdx mod 8).  Numbered XCD by XCD instead, consecutive tiles --
+    // the M tiles of one column block, which read the same code words --
+    // run on one XCD and share its L2.
     const int w = blockIdx.x;
     // work items: whole tiles w, w + P, .. below a.full, then leftover
     // pieces j = w, w + P, .. below a.items
@@ -143,7 +171,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
     // Code words of two groups to LDS: wave instruction b fills 1 KiB =
-    // columns 16 (4 wave + b) .. + 15 of the tile (64 bytes each: the two
+    // columns 16 (CW wave + b) .. + 15 of the tile (64 bytes each: the two
     // groups' 16 words, as four 16-byte chunks q = 2 (group in pair) +
     // half); lane l writes position l & 3 of column (l >> 2), which holds
     // chunk (l & 3) ^ ((column >> 2) & 3), so that 16 lanes reading the
@@ -151,7 +179,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
     unsigned coff[kGemmCDmaPerWave];
 #pragma unroll
     for (int b = 0; b < kGemmCDmaPerWave; ++b) {
-        const unsigned c = 16 * (4 * wave + b) + (lane >> 2);
+        const unsigned c = 16 * (kGemmCDmaPerWave * wave + b) + (lane >> 2);
         coff[b] = c * (unsigned)(a.K / 4) + 16u * ((lane & 3) ^ ((c >> 2) & 3));
     }
     // A operand reads: row 32 i + col, chunk 8 lg + kappa at position
@@ -173,11 +201,11 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         const uint16_t *xtile = a.x + m0 * a.K;
         const unsigned tile_bytes = (unsigned)rows * row_bytes;
 
-        // this lane's scale rows (two sub-tile columns), clamped
-        const uint16_t *srow[2];
+        // this lane's scale rows (one per sub-tile column), clamped
+        const uint16_t *srow[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            int64_t n = n0 + 64 * wave + 32 * j + col;
+        for (int j = 0; j < NJ; ++j) {
+            int64_t n = n0 + 32 * (NJ * wave + j) + col;
             n = n < a.N ? n : a.N - 1;
             srow[j] = a.scales + n * G;
         }
@@ -189,14 +217,17 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         // words of groups g0, g0 + 1 into code slot cs (columns past N read
         // as zero words, their outputs are dropped; a group past the piece
         // reads words that are never used)
+        auto x_rsrc = [&](int g) {
+            return __builtin_amdgcn_make_buffer_rsrc((void *)(xtile + (int64_t)g * kGroup), (short)0,
+                                                     (int)(tile_bytes - 256u * (unsigned)g), (int)kBufferDword3);
+        };
+        auto x_dst = [&](int sb) { return smem + sb * kGemmXBytes + wave * (kGemmDmaPerWave * 1024); };
         auto stage_x = [&](int g, int sb) {
-            __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(xtile + (int64_t)g * kGroup), (short)0, (int)(tile_bytes - 256u * (unsigned)g),
-                (int)kBufferDword3);
-            unsigned char *dst = smem + sb * kGemmXBytes + wave * (kGemmDmaPerWave * 1024);
+            const __amdgpu_buffer_rsrc_t rs = x_rsrc(g);
+            unsigned char *dst = x_dst(sb);
 #pragma unroll
             for (int b = 0; b < kGemmDmaPerWave; ++b)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 1024 * b), 16, voff[b], 0, 0, 0);
+                load_lds16(rs, dst + 1024 * b, voff[b]);
         };
         auto stage_c = [&](int g0, int cs) {
             __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
@@ -205,37 +236,35 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
             unsigned char *cdst = smem + kGemmCBase + cs * kGemmCPairBytes + wave * (kGemmCDmaPerWave * 1024);
 #pragma unroll
             for (int b = 0; b < kGemmCDmaPerWave; ++b)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t *)(cdst + 1024 * b), 16, coff[b], 0, 0, 0);
+                load_lds16(rc, cdst + 1024 * b, coff[b]);
         };
         // this lane's four code words of sub-tile column j, first group of a
         // pair, within a code slot (the second group: chunk position ^ 2)
-        unsigned c_lds[2];
+        unsigned c_lds[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const unsigned c = 64 * wave + 32 * j + col;
+        for (int j = 0; j < NJ; ++j) {
+            const unsigned c = 32 * (NJ * wave + j) + col;
             c_lds[j] = kGemmCBase + c * 64 + 16 * (lg ^ ((c >> 2) & 3));
         }
 
-        f32x16_t T[kGemmMI][2];
+        f32x16_t T[MI][NJ];
 #pragma unroll
-        for (int i = 0; i < kGemmMI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) T[i][jj][v] = 0.0f;
-        float s_c[2];
-        unsigned mask[2];
-        uint32_t s1[2];           // scale bits of group gg + 1
+        float s_c[NJ];
+        unsigned mask[NJ];
+        uint32_t s1[NJ];          // scale bits of group gg + 1
         auto gcl = [&](int g) { return g < kb ? g : kb - 1; };
 
-        // prologue: activations of groups ka and ka + 1 (clamped) into
-        // stages 0 and 1, their code words into slot 0; scales of groups ka
-        // and ka + 1
+        // prologue: activations of group ka into stage 0, the code words of
+        // groups ka and ka + 1 into slot 0; scales of groups ka and ka + 1
         stage_x(ka, 0);
-        stage_x(gcl(ka + 1), 1);
         stage_c(ka, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const float s0 = half_to_float(srow[j][ka]);
             s_c[j] = s0;
             mask[j] = s0 != 0.0f ? kPlaneMask : 0u;
@@ -254,22 +283,26 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
             const unsigned char *ccur = smem + cs * kGemmCPairBytes;
             const bool more = gg + 1 < kb;
             const int g2 = gcl(gg + 2);
-            const int sb2 = sb == 0 ? 2 : sb - 1;            // (sb + 2) % 3
 
-            // scales of group gg + 2 go out first (tiny loads); the stage
-            // of gg + 2 (activations, and the next pair's codes) is issued
-            // mid-group below, so that the waves' loads do not all queue at
-            // the CU's address unit at once
-            uint32_t s2[2];
+            // Scales of group gg + 2 go out first (tiny loads).  The
+            // activations of gg + 1 go into the stage gg - 1 left (all its
+            // reads were consumed before the last barrier), a few loads with
+            // each of the first four MFMA steps, and the next pair's codes
+            // mid-group: issued together, all waves' loads queue at the CU's
+            // address unit and hold up the MFMAs behind them.
+            uint32_t s2[NJ];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) s2[j] = srow[j][g2];
+            for (int j = 0; j < NJ; ++j) s2[j] = srow[j][g2];
+            constexpr int kXPerStep = (kGemmDmaPerWave + 3) / 4;
+            const __amdgpu_buffer_rsrc_t nrs = x_rsrc(gcl(gg + 1));
+            unsigned char *const ndst = x_dst(sb ^ 1);
             __builtin_amdgcn_sched_barrier(0);
 
             // rescale factor to group gg + 1 (its scale arrived a group ago)
-            float r[2];
-            unsigned mask_next[2];
+            float r[NJ];
+            unsigned mask_next[NJ];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const float s_new = half_to_float((uint16_t)s1[j]);
                 const bool nz = __builtin_unpredictable(more && s_new != 0.0f);  // selects, no branch
                 const float ratio = s_c[j] * __builtin_amdgcn_rcpf(s_new);
@@ -278,70 +311,77 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
                 s_c[j] = nz ? s_new : s_c[j];
             }
 
-            u32x4_t cw[2];
+            u32x4_t cw[NJ];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
                 cw[j] = *reinterpret_cast<const u32x4_t *>(ccur + (c_lds[j] ^ (kFirst ? 0u : 32u)));
             const unsigned char *ap = cur + a_row;
             // activation operands one step ahead of the MFMAs that use them
-            bf16x8_t aop[kGemmMI], anx[kGemmMI];
+            bf16x8_t aop[MI], anx[MI];
 #pragma unroll
-            for (int i = 0; i < kGemmMI; ++i)
+            for (int i = 0; i < MI; ++i)
                 aop[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes + 16 * a_sw);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (q == 2) {
+                if (kFirst && q == 2) {
                     __builtin_amdgcn_sched_barrier(0);
-                    stage_x(g2, sb2);
-                    if constexpr (kFirst) stage_c(g2, cs ^ 1);
+                    stage_c(g2, cs ^ 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                unsigned t[2][4];
+                unsigned t[NJ][4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) code_planes(cw[j][q], mask[j], t[j]);
+                for (int j = 0; j < NJ; ++j) code_planes(cw[j][q], mask[j], t[j]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kappa = 2 * q + h;
+                    if (kappa * kXPerStep < kGemmDmaPerWave) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int b = kappa * kXPerStep; b < (kappa + 1) * kXPerStep && b < kGemmDmaPerWave; ++b)
+                            load_lds16(nrs, ndst + 1024 * b, voff[b]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     if (kappa < 7) {
 #pragma unroll
-                        for (int i = 0; i < kGemmMI; ++i)
+                        for (int i = 0; i < MI; ++i)
                             anx[i] = *reinterpret_cast<const bf16x8_t *>(ap + 32 * i * kGemmRowBytes +
                                                                          16 * (a_sw ^ (kappa + 1)));
                     }
-                    bf16x8_t bop[2];
+                    bf16x8_t bop[NJ];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) bop[j] = operand_from_planes(t[j], h);
+                    for (int j = 0; j < NJ; ++j) bop[j] = operand_from_planes(t[j], h);
 #pragma unroll
-                    for (int i = 0; i < kGemmMI; ++i)
+                    for (int i = 0; i < MI; ++i)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
+                        for (int j = 0; j < NJ; ++j) {
                             T[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[j], T[i][j], 0, 0, 0);
                             // Horner step after each tile's last product of the group
                             if (kappa == 7) T[i][j] *= r[j];
                         }
                     if (kappa < 7) {
 #pragma unroll
-                        for (int i = 0; i < kGemmMI; ++i) aop[i] = anx[i];
+                        for (int i = 0; i < MI; ++i) aop[i] = anx[i];
                     }
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 s1[j] = s2[j];
                 mask[j] = mask_next[j];
             }
-            // Everything but this group's stage loads has landed, in
-            // particular the activations of group gg + 1 and, after the
-            // first group of a pair, the codes of the next pair; a plain
-            // barrier (no memory fence, which would wait for those loads
-            // too) publishes them to all waves.  Every LDS read of this
-            // group was consumed above, so the stages refilled next are free.
+            // Everything but the next pair's codes (in flight after the
+            // first group of a pair) has landed: the activations of group
+            // gg + 1 and, after the second group of a pair, the codes of the
+            // next pair.  A plain barrier (no memory fence, which would wait
+            // for the codes too) publishes them to all waves.  Every LDS read
+            // of this group was consumed above, so the stage and code slot
+            // refilled next are free.
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGemmDmaPerWave + (kFirst ? kGemmCDmaPerWave : 0)));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kFirst ? kGemmCDmaPerWave : 0));
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            sb = sb == 2 ? 0 : sb + 1;
+            sb ^= 1;
             if constexpr (!kFirst) cs ^= 1;
         };
         int gg = ka;
@@ -352,14 +392,14 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
         if (gg < kb) group(std::true_type{}, gg);
 
         // epilogue: lane (col, lg) of sub-tile (i, j) holds rows
-        // 32 i + 8 (v >> 2) + 4 lg + (v & 3), column 64 wave + 32 j + col
+        // 32 i + 8 (v >> 2) + 4 lg + (v & 3), column 32 (NJ wave + j) + col
         if (whole) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t n = n0 + 64 * wave + 32 * j + col;
+            for (int j = 0; j < NJ; ++j) {
+                const int64_t n = n0 + 32 * (NJ * wave + j) + col;
                 const float f = -0.5f * s_c[j];
 #pragma unroll
-                for (int i = 0; i < kGemmMI; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * lg + (v & 3);
@@ -367,18 +407,18 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
                     }
             }
         } else {
-            float *out = a.partial + pj * kGemmTileElems + wave * (kGemmMI * 2048) + lane;
+            float *out = a.partial + pj * kGemmTileElems + wave * (MI * NJ * 1024) + lane;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const float f = -0.5f * s_c[j];
 #pragma unroll
-                for (int i = 0; i < kGemmMI; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) out[((i * 2 + j) * 16 + v) * 64] = T[i][j][v] * f;
+                    for (int v = 0; v < 16; ++v) out[((i * NJ + j) * 16 + v) * 64] = T[i][j][v] * f;
             }
         }
-        // the next item's prologue overwrites stages 0 and 1; the last
-        // prefetch of this item may still be landing in one of them
+        // the next item's prologue overwrites the first stages and code
+        // slot 0; the last prefetches of this item may still be landing
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -388,27 +428,26 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
 // grid (leftover tiles, kGemmTileElems / 256) x 256 threads, one output per
 // thread; the piece loads are issued together (up to 8 at a time) and added
 // in K order.
+template <class C>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmArgs a)
 {
     const int64_t lt = blockIdx.x;                 // leftover tile
     const int64_t tile = a.full + lt;
-    const int64_t m0 = (tile % a.tiles_m) * kGemmBM, n0 = (tile / a.tiles_m) * kGemmBN;
+    const int64_t m0 = (tile % a.tiles_m) * C::BM, n0 = (tile / a.tiles_m) * C::BN;
     const int e = blockIdx.y * 256 + threadIdx.x;
     const float *src = a.partial + lt * a.split * kGemmTileElems + e;
     float s = 0.0f;
     for (int p0 = 0; p0 < a.split; p0 += 8) {
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int p = p0 + q < a.split ? p0 + q : a.split - 1;
-            v[q] = src[(int64_t)p * kGemmTileElems];
-        }
+        for (int q = 0; q < 8; ++q)
+            v[q] = p0 + q < a.split ? src[(int64_t)(p0 + q) * kGemmTileElems] : 0.0f;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             if (p0 + q < a.split) s += v[q];
     }
     int mr, nc;
-    gemm_elem_pos(e, mr, nc);
+    gemm_elem_pos<C>(e, mr, nc);
     const int64_t m = m0 + mr, n = n0 + nc;
     if (m < a.M && n < a.N) a.y[m * a.N + n] = s;
 }
@@ -427,6 +466,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *y, int64_t count)
 // workgroup's groups plus the round trip of all partial sums through HBM
 // (the whole GPU moves about 6 MiB in that time).  P workgroups run: C, or
 // fewer when there are fewer work items.
+template <class C>
 GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
 {
     GemmArgs a{};
@@ -434,17 +474,17 @@ GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
     a.N = N;
     a.K = (int)K;
     a.G = (int)(K / kGroup);
-    a.tiles_m = (int)((M + kGemmBM - 1) / kGemmBM);
-    a.tiles = a.tiles_m * ((N + kGemmBN - 1) / kGemmBN);
-    const int64_t C = kGemmWgPerCu * (int64_t)device_cus();
-    const int64_t R = a.tiles / C, r = a.tiles - R * C;
+    a.tiles_m = (int)((M + C::BM - 1) / C::BM);
+    a.tiles = a.tiles_m * ((N + C::BN - 1) / C::BN);
+    const int64_t W = kGemmWgPerCu * (int64_t)device_cus();
+    const int64_t R = a.tiles / W, r = a.tiles - R * W;
     a.split = 1;
     if (r > 0) {
         const double piece_cost = 2.0 * kGemmTileElems * 4 / (6.0 * 1024 * 1024);  // in group times
         double best = 0.0;
         const int smax = a.G / kGemmMinPiece > 1 ? a.G / kGemmMinPiece : 1;
         for (int sp = 1; sp <= smax; ++sp) {
-            const int64_t per_wg = (r * sp + C - 1) / C;                // pieces on the busiest workgroup
+            const int64_t per_wg = (r * sp + W - 1) / W;                // pieces on the busiest workgroup
             const int64_t longest = (a.G + sp - 1) / sp;
             const double t = (double)(R * a.G + per_wg * longest) + (sp > 1 ? piece_cost * (double)(r * sp) : 0.0);
             if (sp == 1 || t < best) {
@@ -456,16 +496,18 @@ GemmArgs plan_gemm(int64_t M, int64_t N, int64_t K)
     if (a.split == 1) {  // every tile done whole
         a.full = a.tiles;
         a.items = 0;
-        a.P = (int)(a.tiles < C ? a.tiles : C);
+        a.P = (int)(a.tiles < W ? a.tiles : W);
     } else {
-        a.full = R * C;
+        a.full = R * W;
         a.items = r * a.split;
-        a.P = (int)(R > 0 || a.items >= C ? C : a.items);
+        a.P = (int)(R > 0 || a.items >= W ? W : a.items);
     }
     return a;
 }
 
 bool gemm_splits_tiles(const GemmArgs &a) { return a.items > 0; }
+
+typedef GemmTile GemmUse;  // the tile shape every call runs
 
 }  // namespace
 
@@ -515,7 +557,7 @@ namespace tern {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    const GemmArgs a = plan_gemm(M, N, K);
+    const GemmArgs a = plan_gemm<GemmUse>(M, N, K);
     return gemm_splits_tiles(a) ? (size_t)a.items * kGemmTileElems * sizeof(float) : 0;
 }
 
@@ -532,19 +574,19 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
                            st, y, count);
         return (int)hipGetLastError();
     }
-    GemmArgs a = plan_gemm(M, N, K);
+    GemmArgs a = plan_gemm<GemmUse>(M, N, K);
     a.x = static_cast<const uint16_t *>(x);
     a.codes = codes;
     a.scales = scales;
     a.y = y;
     a.partial = static_cast<float *>(workspace);
-    const size_t lds = kGemmLdsBytes;
-    int rc = ensure_lds(gemm_kernel, lds);
+    const size_t lds = GemmUse::kLdsBytes;
+    int rc = ensure_lds(gemm_kernel<GemmUse>, lds);
     if (rc) return rc;
-    hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
+    hipLaunchKernelGGL(gemm_kernel<GemmUse>, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
     rc = (int)hipGetLastError();
     if (rc || !gemm_splits_tiles(a)) return rc;
-    hipLaunchKernelGGL(gemm_fixup_kernel, dim3((unsigned)(a.items / a.split), kGemmTileElems / 256), dim3(256),
+    hipLaunchKernelGGL(gemm_fixup_kernel<GemmUse>, dim3((unsigned)(a.items / a.split), kGemmTileElems / 256), dim3(256),
                        0, st, a);
     return (int)hipGetLastError();
 }
