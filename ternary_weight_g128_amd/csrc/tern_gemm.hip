@@ -113,6 +113,7 @@ struct GemmArgs {
     int64_t full;           // R * P: tiles done whole, round robin
     int split;              // s: K pieces of each leftover tile (1: none left)
     int64_t items;          // r * s leftover pieces
+    bool y_vec;             // y 16-byte aligned and N % 4 == 0
 };
 
 // One 16-byte buffer load per lane straight into LDS (lane l writes dst +
@@ -425,23 +426,26 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
 }
 
 // Leftover tiles: y = sum of their a.split K pieces, in K order.
-// grid (leftover tiles, kGemmTileElems / 256) x 256 threads, one output per
-// thread; the piece loads are issued together (up to 8 at a time) and added
-// in K order.
+// grid (leftover tiles, kGemmTileElems / 1024) x 256 threads, four outputs
+// per thread: elements 4t .. 4t + 3 of the register order are four
+// consecutive columns of one row, so they are one 16-byte load per piece and
+// one 16-byte store.  The piece loads are issued together (up to 8 at a
+// time) and added in K order.
 template <class C>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmArgs a)
 {
     const int64_t lt = blockIdx.x;                 // leftover tile
     const int64_t tile = a.full + lt;
     const int64_t m0 = (tile % a.tiles_m) * C::BM, n0 = (tile / a.tiles_m) * C::BN;
-    const int e = blockIdx.y * 256 + threadIdx.x;
-    const float *src = a.partial + lt * a.split * kGemmTileElems + e;
-    float s = 0.0f;
+    const int e = 4 * (blockIdx.y * 256 + threadIdx.x);
+    const f32x4_t *src = reinterpret_cast<const f32x4_t *>(a.partial + lt * a.split * kGemmTileElems + e);
+    constexpr int kPieceVecs = kGemmTileElems / 4;
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < a.split; p0 += 8) {
-        float v[8];
+        f32x4_t v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            v[q] = p0 + q < a.split ? src[(int64_t)(p0 + q) * kGemmTileElems] : 0.0f;
+            v[q] = p0 + q < a.split ? src[(int64_t)(p0 + q) * kPieceVecs] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             if (p0 + q < a.split) s += v[q];
@@ -449,7 +453,15 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmArgs a)
     int mr, nc;
     gemm_elem_pos<C>(e, mr, nc);
     const int64_t m = m0 + mr, n = n0 + nc;
-    if (m < a.M && n < a.N) a.y[m * a.N + n] = s;
+    if (m >= a.M) return;
+    float *yp = a.y + m * a.N + n;
+    if (a.y_vec && n + 3 < a.N) {
+        *reinterpret_cast<f32x4_t *>(yp) = s;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (n + c < a.N) yp[c] = s[c];
+    }
 }
 
 // K = 0: y = 0 (an empty sum).
@@ -586,7 +598,8 @@ int launch_gemm(const void *x, int64_t M, int64_t K, const uint32_t *codes, cons
     hipLaunchKernelGGL(gemm_kernel<GemmUse>, dim3((unsigned)a.P), dim3(kGemmThreads), lds, st, a);
     rc = (int)hipGetLastError();
     if (rc || !gemm_splits_tiles(a)) return rc;
-    hipLaunchKernelGGL(gemm_fixup_kernel<GemmUse>, dim3((unsigned)(a.items / a.split), kGemmTileElems / 256), dim3(256),
+    a.y_vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && N % 4 == 0;
+    hipLaunchKernelGGL(gemm_fixup_kernel<GemmUse>, dim3((unsigned)(a.items / a.split), kGemmTileElems / 1024), dim3(256),
                        0, st, a);
     return (int)hipGetLastError();
 }
