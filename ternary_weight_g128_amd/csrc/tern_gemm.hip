@@ -152,27 +152,24 @@ __global__ __launch_bounds__(kGemmThreads, kGemmWgPerCu) void gemm_kernel(const 
     const int64_t KW = a.K / 16;
     const unsigned row_bytes = 2u * (unsigned)a.K;
 
-    // The hardware deals workgroups to the eight XCDs round robin
-    // (blockIdx mod 8).  Numbered XCD by XCD instead, consecutive tiles --
-    // the M tiles of one column block, which read the same code words --
-    // run on one XCD and share its L2.
     const int w = blockIdx.x;
     // work items: whole tiles w, w + P, .. below a.full, then leftover
     // pieces j = w, w + P, .. below a.items
     const int64_t n_full = w < a.full % a.P ? a.full / a.P + 1 : a.full / a.P;
     const int64_t n_part = a.items > w ? (a.items - 1 - w) / a.P + 1 : 0;
 
-    // Loads to LDS: wave instruction b fills 1 KiB = rows 4 (DW wave + b) ..
-    // + 3 of a stage; lane l writes position l & 15 of its row, i.e. chunk
-    // (l & 15) ^ (row & 15) of that row.
+    // Loads to LDS (D = kGemmDmaPerWave per wave): wave instruction b fills
+    // 1 KiB = rows 4 (D wave + b) .. + 3 of a stage; lane l writes position
+    // l & 15 of its row, i.e. chunk (l & 15) ^ (row & 15) of that row.
     unsigned voff[kGemmDmaPerWave];
 #pragma unroll
     for (int b = 0; b < kGemmDmaPerWave; ++b) {
         const unsigned r = 4 * (kGemmDmaPerWave * wave + b) + (lane >> 4);
         voff[b] = r * row_bytes + 16u * ((lane & 15) ^ (r & 15));
     }
-    // Code words of two groups to LDS: wave instruction b fills 1 KiB =
-    // columns 16 (CW wave + b) .. + 15 of the tile (64 bytes each: the two
+    // Code words of two groups to LDS (D' = kGemmCDmaPerWave per wave): wave
+    // instruction b fills 1 KiB = columns 16 (D' wave + b) .. + 15 of the
+    // tile (64 bytes each: the two
     // groups' 16 words, as four 16-byte chunks q = 2 (group in pair) +
     // half); lane l writes position l & 3 of column (l >> 2), which holds
     // chunk (l & 3) ^ ((column >> 2) & 3), so that 16 lanes reading the
