@@ -452,8 +452,9 @@ def _gemm_sampled(tern, oracle_lib, M, K, N, seed, t, s, x, cols, what):
 
 @pytest.mark.parametrize("M,K,N", [
     (600, 4096, 700),    # ragged row and column tiles; every tile split in pieces
-    (1024, 512, 1024),   # ranges of exactly one tile: no pieces, no workspace
-    (4000, 384, 3900),   # ranges of 5-6 groups: whole tiles mixed with pieces
+    (1024, 512, 1024),   # fewer tiles than workgroups, too short to split: no workspace
+    (4000, 384, 3900),   # two rounds of whole tiles for some workgroups, K shorter than a piece
+    (2300, 1024, 3700),  # one round of whole tiles, then the leftover tiles in K pieces (ragged)
     (300, 17408, 96),    # long K split over many workgroups
 ])
 def test_gemm_work_split_cases(tern, oracle_lib, M, K, N):
