@@ -57,7 +57,7 @@ typedef enum tern_status {
     TERN_EINVAL = 1,        /* bad size, pointer, alignment or non-finite scale */
     TERN_ENOTTERNARY = 2,   /* input values are not ternary-g128 */
     TERN_EBADCODE = 3,      /* a 2-bit slot holds the unused value 3 */
-    TERN_EUNSUPPORTED = 4,  /* valid request this build does not implement */
+    TERN_EUNSUPPORTED = 4,  /* valid request that the library does not implement */
     TERN_EDEVICE = 5        /* HIP runtime error */
 } tern_status;
 
