@@ -124,7 +124,7 @@ def _gemm(tern, x=A16, xdt=1, M=64, K=128, codes=A16, scales=A16, N=16, y=A16, w
 
 @pytest.mark.parametrize("kw,status", [
     (dict(xdt=0), 4), (dict(xdt=3), 4), (dict(K=64), 1), (dict(M=-2), 1),
-    (dict(x=NULL), 1), (dict(y=A2), 1), (dict(codes=A2), 1),
+    (dict(x=NULL), 1), (dict(y=A2), 1), (dict(codes=A2), 1), (dict(K=1 << 22), 1),
 ])
 def test_gemm_rejects(tern, kw, status):
     assert _gemm(tern, **kw) == status

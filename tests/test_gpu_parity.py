@@ -537,6 +537,22 @@ def test_gemm_k_zero_and_empty(tern):
     T.cuda.synchronize()
 
 
+def test_gemm_at_the_k_limit(tern, oracle_lib):
+    """K = 2^22 - 128, the largest K tern_gemm takes (32-bit buffer offsets
+    over a 128-row tile of x): one ragged tile split along K over many
+    workgroups, every element against the oracle."""
+    M, K, N, seed = 3, (1 << 22) - 128, 40, 97
+    print(f"gemm K limit M={M} K={K} N={N} ws={tern.tern_gemm_workspace_bytes(M, N, K)}", flush=True)
+    t = synth.ternary(seed, N, K, 0.35)
+    s = synth.scales_f16(seed, N, K)
+    x = synth.activations_bf16(seed, M, K, outlier_frac=0.01)
+    codes_d, scales_d = pack_to_device(tern, t, s)
+    y = tern.tern_gemm(x_to_device(x), codes_d, scales_d)
+    torch().cuda.synchronize()
+    y_ref, bound = oracle_lib.matmul(x, oracle_lib.encode(t), s, K, threads=oracle_threads(oracle_lib))
+    assert_matmul_close(y_to_host(y), y_ref, bound, what=f"gemm K{K}")
+
+
 @pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (33, 1280), (1000, 5120)])
 def test_pack_device_matches_oracle_encode(tern, oracle_lib, N, K):
     """Device packer: bit-exact against the oracle's encoder."""
