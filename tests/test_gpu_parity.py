@@ -293,6 +293,23 @@ def test_fwht_matches_oracle(tern, oracle_lib, M, K, block, xdt, signed):
     assert_fwht_close(y_to_host(yi), x64, what="round trip")
 
 
+@pytest.mark.parametrize("K,block", [(4096, 4096), (64, 64), (32, 4)])
+def test_fwht_rows_past_the_grid_limit(tern, oracle_lib, K, block):
+    """More rows than one grid dimension holds (65,535): the workgroups loop
+    over rows.  Rows on both sides of the limit, and the rows that share a
+    workgroup with them, are checked against the oracle (rows are
+    independent)."""
+    M, seed = 65535 + 7, 71 + K
+    print(f"fwht rows M={M} K={K} block={block}", flush=True)
+    x = synth.activations_bf16(seed, M, K)
+    d = synth.signs(seed, K)
+    y = tern.tern_fwht(x_to_device(x), torch().from_numpy(d).cuda(), block)
+    torch().cuda.synchronize()
+    rows = np.array([0, 1, 6, 7, 65533, 65534, 65535, 65536, M - 1])
+    yh = y[torch().from_numpy(rows).cuda()].cpu().numpy()
+    assert_fwht_close(yh, oracle_lib.fwht(oracle_lib.bf16_bits_to_f64(x[rows]), d, block), what=f"rows K{K}")
+
+
 def test_fwht_in_place(tern, oracle_lib):
     T = torch()
     x = synth.activations_f32(3, 2, 8192)
